@@ -1,0 +1,452 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+Each test checks an oracle function against something it does not compute
+itself: a worked example printed on (or derived by hand from) the pages, a
+closed form, an exhaustive enumeration, integer arithmetic, or the definition
+of uniform quantization. ``test_planted_mistakes`` plants plausible bugs in a
+copy of the oracle and checks that these pins catch each of them.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bcq as ob
+from conftest import load_golden
+
+# ---------------------------------------------------------------- helpers
+
+def _encode_signs(sign_matrix):
+    """+-1 matrix [..., K] -> sign bytes [..., K/8], written element by element.
+
+    Encoding is done with explicit integer bit arithmetic (bit k%8 of byte k//8),
+    independent of numpy's packbits/unpackbits used inside the oracle.
+    """
+    s = np.asarray(sign_matrix)
+    K = s.shape[-1]
+    out = np.zeros(s.shape[:-1] + (K // 8,), np.uint8)
+    it = np.nditer(s[..., 0], flags=["multi_index"])
+    for _ in it:
+        lead = it.multi_index
+        for k in range(K):
+            if s[lead + (k,)] > 0:
+                out[lead + (k // 8,)] |= np.uint8(1 << (k % 8))
+    return out
+
+
+def _int_bcq_problem(rng, N, K, q, g, m, with_offset):
+    """A BCQ matrix whose weights are integers known independently of the oracle.
+
+    Plane scales are alpha_i = 2^i * gamma[j, grp] with integer gamma, so each
+    weight equals gamma * odd + delta where odd is the odd integer whose binary
+    digits (shifted) are the sign bits. Returns the pieces and the integer W.
+    """
+    G = K // g
+    odd = rng.integers(0, 1 << q, size=(N, K)) * 2 - ((1 << q) - 1)     # odd ints in [-(2^q-1), 2^q-1]
+    digits = (odd + (1 << q) - 1) // 2                                    # in [0, 2^q)
+    gamma = rng.integers(-3, 4, size=(N, G))
+    delta = rng.integers(-5, 6, size=(N, G)) if with_offset else np.zeros((N, G), np.int64)
+    W = np.repeat(gamma, g, axis=1) * odd + np.repeat(delta, g, axis=1)
+    planes = np.stack([np.where((digits >> i) & 1, 1, -1) for i in range(q)])
+    bits = _encode_signs(planes)
+    alpha = np.stack([(gamma * (1 << i)) for i in range(q)]).astype(np.float16)
+    offset = delta.astype(np.float16) if with_offset else None
+    x = rng.integers(-8, 9, size=(m, K))
+    return bits, alpha, offset, x.astype(np.float16), W, x
+
+
+# ---------------------------------------------------------------- golden
+
+def test_sign_order_golden():
+    fx = load_golden("sign_order_example.json")
+    for case in fx["cases"]:
+        bits = np.array(case["bits"], np.uint8)
+        alpha = np.array(case["alpha"], np.float16)
+        off = np.array(case["offset"], np.float16) if "offset" in case else None
+        x = np.array(case["x"], np.float16)[None, :]
+        s = ob.signs(bits)
+        assert np.array_equal(s.reshape(len(case["signs"]), -1), np.array(case["signs"]))
+        y, bound = ob.gemv(bits, alpha, off, x, case["g"])
+        assert y.shape == (1, 1)
+        assert y[0, 0] == case["y"]
+        assert ob.gemv_lut(bits, alpha, off, x, case["g"])[0, 0] == case["y"]
+
+
+def test_lut_entries_golden():
+    fx = load_golden("lut_entries_example.json")
+    t = ob.lut_table(fx["x"])
+    for p, v in fx["entries"].items():
+        assert t[int(p)] == v
+
+
+def test_uniform_rewrite_golden():
+    fx = load_golden("uniform_rewrite_example.json")
+    codes = np.array(fx["codes"], np.uint8)
+    scale = np.array(fx["scale"], np.float16)
+    zero = np.array(fx["zero"], np.uint8)
+    bits, alpha, off, n_r = ob.uniform_to_bcq(codes, scale, zero, fx["q"], fx["g"])
+    assert n_r == 0
+    assert np.array_equal(alpha.astype(np.float64), np.array(fx["alpha"]))
+    assert np.array_equal(off.astype(np.float64), np.array(fx["offset"]))
+    assert np.array_equal(ob.signs(bits)[:, :, :4], np.array(fx["plane_signs"]))
+    # pad K to 8 is not needed for the decode check above; rebuild with K=8
+    w = ob.dequant_uniform(codes, scale, zero, fx["g"])
+    assert np.array_equal(w, np.array(fx["weights"]))
+
+
+def test_footprint_golden():
+    fx = load_golden("footprint_example.json")
+    for c in fx["cases"]:
+        assert ob.footprint_bits(c["n"], c["q"], c["g"], c["offset"]) == c["bits"]
+    # the page's point: the lower bit width costs more storage here
+    a, b = fx["cases"]
+    assert a["q"] < b["q"] and ob.footprint_bits(a["n"], a["q"], a["g"]) > ob.footprint_bits(b["n"], b["q"], b["g"])
+
+
+def test_opt175b_size_consistency():
+    fx = load_golden("opt175b_size.json")
+    K, q = fx["K"], fx["q"]
+    n = 10 ** 6 * K        # any multiple of K; the ratio is per weight
+    ratio = 16 * n / ob.footprint_bits(n, q, K)
+    assert round(ratio, 2) == fx["ratio"]
+    assert round(fx["fp16_gb"] / ratio, 1) == fx["q3_gb"]
+    # group size 128 would not reproduce the page's figure
+    assert round(16 * n / ob.footprint_bits(n, q, 128), 2) != fx["ratio"]
+
+
+# ---------------------------------------------------------------- tables
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lut_closed_forms(seed):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-1000, 1001, size=8).astype(np.float64)   # exact in fp64
+    t = ob.lut_table(x)
+    total = x.sum()
+    for p in range(256):
+        chosen = sum(x[k] for k in range(8) if (p >> k) & 1)
+        assert t[p] == 2 * chosen - total            # closed form
+        assert t[p ^ 0xFF] == -t[p]                  # complement symmetry
+    assert t[0xFF] == total and t[0] == -total
+    for k in range(8):
+        assert t[1 << k] == 2 * x[k] - total
+
+
+# ---------------------------------------------------------------- brute force
+
+def test_bruteforce_all_patterns_q2():
+    """N=1, K=8, q=2: all 2^16 sign patterns (one per row) against integer sums."""
+    x = np.array([3, -1, 4, 1, -5, 9, 2, -6], np.float16)
+    xi = [3, -1, 4, 1, -5, 9, 2, -6]
+    pats = [(a, b) for a in range(256) for b in range(256)]
+    bits = np.array([[[a] for a, _ in pats], [[b] for _, b in pats]], np.uint8)   # [2][65536][1]
+    alpha = np.ones((2, len(pats), 1), np.float16)
+    alpha[1] = 2.0
+    w = ob.reconstruct_rows(bits, alpha, None, 8, np.arange(len(pats)))
+    y, _ = ob.gemv(bits, alpha, None, x[None], 8, block=4096)
+    for r, (a, b) in enumerate(pats):
+        expect = [(1 if (a >> k) & 1 else -1) + 2 * (1 if (b >> k) & 1 else -1) for k in range(8)]
+        assert w[r].tolist() == expect
+        assert y[0, r] == sum(e * v for e, v in zip(expect, xi))
+    sub = np.arange(0, len(pats), 257)
+    y_lut = ob.gemv_lut(bits[:, sub], alpha[:, sub], None, x[None], 8)
+    assert np.array_equal(y_lut[0], y[0, sub])
+
+
+@pytest.mark.parametrize("N,K,q,g,m,off", [
+    (3, 16, 1, 8, 1, False),
+    (4, 32, 2, 16, 2, True),
+    (5, 64, 3, 32, 1, True),
+    (2, 24, 4, 24, 3, False),
+    (7, 40, 8, 8, 1, True),
+])
+def test_integer_weights_exact(N, K, q, g, m, off):
+    rng = np.random.default_rng(N * 100 + K + q)
+    bits, alpha, offset, x16, W, xi = _int_bcq_problem(rng, N, K, q, g, m, off)
+    w = ob.reconstruct_rows(bits, alpha, offset, g, np.arange(N))
+    assert np.array_equal(w, W.astype(np.float64))
+    y, bound = ob.gemv(bits, alpha, offset, x16, g)
+    assert np.array_equal(y, (xi @ W.T).astype(np.float64))
+    assert np.array_equal(bound, (np.abs(xi) @ np.abs(W).T).astype(np.float64))
+    assert np.array_equal(ob.gemv_lut(bits, alpha, offset, x16, g), y)
+
+
+def test_gemv_rows_and_blocks():
+    rng = np.random.default_rng(7)
+    bits, alpha, offset, x16, W, xi = _int_bcq_problem(rng, 37, 64, 3, 16, 2, True)
+    y_all, _ = ob.gemv(bits, alpha, offset, x16, 16, block=5)
+    rows = np.array([36, 0, 17, 5])
+    y_sel, _ = ob.gemv(bits, alpha, offset, x16, 16, rows=rows, block=3)
+    assert np.array_equal(y_sel, y_all[:, rows])
+    assert np.array_equal(y_all, (xi @ W.T).astype(np.float64))
+
+
+def test_unit_vector_probes_and_zero():
+    rng = np.random.default_rng(11)
+    q, N, K, g = 3, 6, 32, 16
+    bits = rng.integers(0, 256, size=(q, N, K // 8), dtype=np.uint8)
+    alpha = (np.abs(rng.standard_normal((q, N, K // g))) * 0.02).astype(np.float16)
+    w = ob.reconstruct_rows(bits, alpha, None, g, np.arange(N))
+    for k in range(K):
+        e = np.zeros((1, K), np.float16)
+        e[0, k] = 1
+        y, _ = ob.gemv(bits, alpha, None, e, g)
+        # column k: sum_i alpha * sign, the sign read straight from the byte
+        col = np.array([sum(float(alpha[i, j, k // g]) * (1 if (int(bits[i, j, k // 8]) >> (k % 8)) & 1 else -1)
+                            for i in range(q)) for j in range(N)])
+        assert np.array_equal(y[0], col)
+        assert np.array_equal(w[:, k], col)
+    y0, b0 = ob.gemv(bits, alpha, None, np.zeros((1, K), np.float16), g)
+    assert not y0.any() and not b0.any()
+
+
+def test_random_lut_vs_direct():
+    rng = np.random.default_rng(5)
+    for (N, K, q, g, m, off) in [(5, 64, 3, 32, 2, True), (3, 128, 2, 128, 1, False)]:
+        bits = rng.integers(0, 256, size=(q, N, K // 8), dtype=np.uint8)
+        alpha = (np.abs(rng.standard_normal((q, N, K // g))) * 0.02).astype(np.float16)
+        offset = (rng.standard_normal((N, K // g)) * 0.02).astype(np.float16) if off else None
+        x = rng.standard_normal((m, K)).astype(np.float16)
+        y, bound = ob.gemv(bits, alpha, offset, x, g)
+        y2 = ob.gemv_lut(bits, alpha, offset, x, g)
+        assert np.allclose(y, y2, rtol=0, atol=1e-12 * (1 + bound.max()))
+
+
+# ---------------------------------------------------------------- uniform -> BCQ
+
+@pytest.mark.parametrize("q", range(1, 9))
+def test_uniform_rewrite_exhaustive(q):
+    """Every (code, zero-point) pair at unit scale: the BCQ form equals c - z exactly."""
+    n = 1 << q
+    codes = np.repeat(np.arange(n, dtype=np.uint8)[None, :], n, axis=0)      # [z][c]
+    Kp = -(-n // 8) * 8
+    codes_p = np.zeros((n, Kp), np.uint8)
+    codes_p[:, :n] = codes
+    g = Kp
+    scale = np.ones((n, 1), np.float16)
+    zero = np.arange(n, dtype=np.uint8)[:, None]
+    bits, alpha, off, n_r = ob.uniform_to_bcq(codes_p, scale, zero, q, g)
+    assert n_r == 0
+    w = ob.reconstruct_rows(bits, alpha, off, g, np.arange(n))
+    expect = codes_p.astype(np.int64) - np.arange(n)[:, None]
+    assert np.array_equal(w, expect.astype(np.float64))
+
+
+def _count_inexact_half(scale16, q, zero):
+    """Groups whose rewritten values cannot all be fp16, counted from bit patterns.
+
+    For q=4, z=8 the rewrite needs s/2 (alpha_0 and -offset) besides s, 2s, 4s.
+    s/2 is an fp16 value unless s < 2^-13 and s is an odd multiple of 2^-24.
+    """
+    assert q == 4 and zero == 8
+    u = scale16.view(np.uint16).astype(np.int64) & 0x7FFF
+    exp_field = u >> 10
+    small = exp_field == 0                       # subnormal: s = mant * 2^-24
+    odd = (u & 1) == 1
+    return int(np.count_nonzero(small & odd))
+
+
+def test_uniform_rewrite_int4_scales():
+    rng = np.random.default_rng(3)
+    N, K, g = 64, 256, 128
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    scale = (np.abs(rng.standard_normal((N, K // g))) * 0.01).astype(np.float16)
+    # force a few tiny odd subnormal scales, and a zero scale
+    scale.view(np.uint16)[:4, 0] = [1, 3, 0x03FF, 2]
+    scale[5, 1] = 0
+    zero = np.full((N, K // g), 8, np.uint8)
+    bits, alpha, off, n_r = ob.uniform_to_bcq(codes, scale, zero, 4, g)
+    assert n_r == _count_inexact_half(scale, 4, 8)
+    w_bcq = ob.reconstruct_rows(bits, alpha, off, g, np.arange(N))
+    w_def = ob.dequant_uniform(codes, scale, zero, g)
+    s_u = scale.view(np.uint16).astype(np.int64)
+    exact_grp = ~(((s_u & 0x7C00) == 0) & ((s_u & 1) == 1))
+    exact_el = np.repeat(exact_grp, g, axis=1)
+    assert np.array_equal(w_bcq[exact_el], w_def[exact_el])
+    # rounded groups: each of alpha_0 and offset is off by at most half a subnormal step
+    assert np.all(np.abs(w_bcq - w_def)[~exact_el] <= 2.0 ** -24)
+
+
+def test_uniform_rewrite_rejects():
+    codes = np.zeros((1, 8), np.uint8)
+    with pytest.raises(ValueError):
+        ob.uniform_to_bcq(codes + 16, np.ones((1, 1), np.float16), np.zeros((1, 1), np.uint8), 4, 8)
+    with pytest.raises(ValueError):
+        ob.uniform_to_bcq(codes, np.ones((1, 1), np.float16), np.full((1, 1), 16, np.uint8), 4, 8)
+    with pytest.raises(ValueError):
+        ob.uniform_to_bcq(codes, np.full((1, 1), np.inf, np.float16), np.zeros((1, 1), np.uint8), 4, 8)
+    with pytest.raises(ValueError):   # 4 * 60000 overflows fp16
+        ob.uniform_to_bcq(codes, np.full((1, 1), 60000, np.float16), np.zeros((1, 1), np.uint8), 4, 8)
+
+
+# ---------------------------------------------------------------- packed layout
+
+def _unpack_by_reshape(pb, pa, po, q, N, K, g):
+    """Inverse of the packed layout written with reshapes/transposes (not loops)."""
+    RT = -(-N // 16)
+    C = K // 8
+    KT = -(-C // 64)
+    G = K // g
+    b = pb.reshape(RT, KT, q, 64, 16).transpose(2, 0, 4, 1, 3).reshape(q, RT * 16, KT * 64)
+    a = pa.reshape(RT, G, q, 16).transpose(2, 0, 3, 1).reshape(q, RT * 16, G)
+    o = po.reshape(RT, G, 16).transpose(0, 2, 1).reshape(RT * 16, G) if po.size else None
+    return b[:, :N, :C], b, a[:, :N, :], a, (o[:N] if o is not None else None), o
+
+
+@pytest.mark.parametrize("N,K,q,g,off", [(17, 520, 3, 8, True), (16, 512, 1, 512, False),
+                                         (40, 1024, 4, 128, True), (1, 8, 2, 8, False)])
+def test_pack_roundtrip(N, K, q, g, off):
+    rng = np.random.default_rng(N + K)
+    bits = rng.integers(0, 256, size=(q, N, K // 8), dtype=np.uint8)
+    alpha = rng.standard_normal((q, N, K // g)).astype(np.float16)
+    offset = rng.standard_normal((N, K // g)).astype(np.float16) if off else None
+    pb, pa, po = ob.pack(bits, alpha, offset, g)
+    nb, na, no = ob.packed_sizes(N, K, q, g, off)
+    assert pb.size == nb and pa.size == na and po.size == no
+    b, b_full, a, a_full, o, o_full = _unpack_by_reshape(pb, pa, po, q, N, K, g)
+    assert np.array_equal(b, bits)
+    assert np.array_equal(a, alpha.view(np.uint16))
+    # padding is zero
+    assert not b_full[:, N:, :].any() and not b_full[:, :, K // 8:].any()
+    assert not a_full[:, N:, :].any()
+    if off:
+        assert np.array_equal(o, offset.view(np.uint16))
+        assert not o_full[N:].any()
+
+
+def test_pack_single_bit_positions():
+    """Hand-placed bytes land where the layout definition says."""
+    q, N, K, g = 2, 20, 1024, 256
+    bits = np.zeros((q, N, K // 8), np.uint8)
+    # (plane, row, chunk) -> expected flat index: ((rt*KT + kt)*q + i)*1024 + c*16 + r
+    cases = {(1, 17, 70): ((1 * 2 + 1) * 2 + 1) * 1024 + 6 * 16 + 1,
+             (0, 0, 0): 0,
+             (0, 15, 63): 63 * 16 + 15,
+             (1, 3, 127): ((0 * 2 + 1) * 2 + 1) * 1024 + 63 * 16 + 3}
+    for n, (i, j, c) in enumerate(cases):
+        bits[i, j, c] = n + 1
+    alpha = np.zeros((q, N, K // g), np.float16)
+    alpha[1, 18, 3] = 1.0          # rt 1, grp 3, plane 1, row 2 -> ((1*4+3)*2+1)*16 + 2
+    pb, pa, _ = ob.pack(bits, alpha, None, g)
+    for n, (key, idx) in enumerate(cases.items()):
+        assert pb[idx] == n + 1
+    assert np.count_nonzero(pb) == len(cases)
+    assert pa[((1 * 4 + 3) * 2 + 1) * 16 + 2] == np.float16(1.0).view(np.uint16)
+    assert np.count_nonzero(pa) == 1
+
+
+# ---------------------------------------------------------------- the checker itself
+
+def test_parity_rule():
+    ref = np.array([[1.0, -2.0, 0.0]])
+    bound = np.array([[10.0, 10.0, 0.0]])
+    ok, worst = ob.parity_ok(ref + np.array([[0.0100, -0.0100, 0.0001]]), ref, bound)
+    assert ok and worst <= 1.0
+    ok, _ = ob.parity_ok(ref + np.array([[0.0102, 0.0, 0.0]]), ref, bound)
+    assert not ok
+    ok, _ = ob.parity_ok(ref + np.array([[0.0, 0.0, 0.00011]]), ref, bound)
+    assert not ok
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _run_pins():
+    """The pins above, as a callable that raises AssertionError on any failure."""
+    test_sign_order_golden()
+    test_lut_entries_golden()
+    test_uniform_rewrite_golden()
+    test_footprint_golden()
+    test_integer_weights_exact(5, 64, 3, 32, 1, True)
+    test_integer_weights_exact(7, 40, 8, 8, 1, True)
+    test_unit_vector_probes_and_zero()
+    test_uniform_rewrite_exhaustive(4)
+    test_pack_roundtrip(17, 520, 3, 8, True)
+    test_pack_single_bit_positions()
+
+
+def _mut_signs_msb_first(bits):
+    b01 = np.unpackbits(np.asarray(bits, dtype=np.uint8), axis=-1, bitorder="big")
+    return (b01.astype(np.int8) * 2 - 1).astype(np.int8)
+
+
+def _mut_signs_flipped(bits):
+    b01 = np.unpackbits(np.asarray(bits, dtype=np.uint8), axis=-1, bitorder="little")
+    return (1 - b01.astype(np.int8) * 2).astype(np.int8)
+
+
+_orig_reconstruct = ob.reconstruct_rows
+
+
+def _mut_reconstruct_drop_offset(bits, alpha, offset, g, rows):
+    return _orig_reconstruct(bits, alpha, None, g, rows)
+
+
+def _mut_reconstruct_group_modulo(bits, alpha, offset, g, rows):
+    # wrong group index: k % G instead of k // g
+    q = bits.shape[0]
+    b = ob.signs(bits[:, rows, :]).astype(np.float64)
+    K = b.shape[-1]
+    G = alpha.shape[-1]
+    a = alpha[:, rows, :].astype(np.float64)
+    a_full = np.tile(a, (1, 1, K // G))
+    w = sum(a_full[i] * b[i] for i in range(q))
+    if offset is not None:
+        w = w + np.tile(offset[rows, :].astype(np.float64), (1, K // G))
+    return w
+
+
+def _mut_reconstruct_last_plane_dropped(bits, alpha, offset, g, rows):
+    return _orig_reconstruct(bits[:-1], alpha[:-1], offset, g, rows) if bits.shape[0] > 1 else \
+        _orig_reconstruct(bits, alpha * 0, offset, g, rows)
+
+
+_orig_lut = ob.lut_table
+
+
+def _mut_lut_wrong_sign(xc):
+    return -_orig_lut(xc)
+
+
+_orig_u2b = ob.uniform_to_bcq
+
+
+def _mut_u2b_offset_sign(codes, scale, zero, q, g):
+    bits, a, o, n = _orig_u2b(codes, scale, zero, q, g)
+    return bits, a, (-o.astype(np.float64)).astype(np.float16), n
+
+
+def _mut_u2b_alpha_scale(codes, scale, zero, q, g):
+    bits, a, o, n = _orig_u2b(codes, scale, zero, q, g)
+    return bits, (a.astype(np.float64) * 2).astype(np.float16), o, n
+
+
+def _mut_footprint_no_scales(n, q, g, offset=False):
+    return q * n
+
+
+_orig_pack = ob.pack
+
+
+def _mut_pack_rows_chunks_swapped(bits, alpha, offset, g):
+    pb, pa, po = _orig_pack(bits, alpha, offset, g)
+    q, N, C = bits.shape
+    RT, KT = -(-N // 16), -(-C // 64)
+    pb = pb.reshape(RT, KT, q, 64, 16).transpose(0, 1, 2, 4, 3).reshape(-1).copy()
+    return pb, pa, po
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("signs", _mut_signs_msb_first),
+    ("signs", _mut_signs_flipped),
+    ("reconstruct_rows", _mut_reconstruct_drop_offset),
+    ("reconstruct_rows", _mut_reconstruct_group_modulo),
+    ("reconstruct_rows", _mut_reconstruct_last_plane_dropped),
+    ("lut_table", _mut_lut_wrong_sign),
+    ("uniform_to_bcq", _mut_u2b_offset_sign),
+    ("uniform_to_bcq", _mut_u2b_alpha_scale),
+    ("footprint_bits", _mut_footprint_no_scales),
+    ("pack", _mut_pack_rows_chunks_swapped),
+])
+def test_planted_mistakes(monkeypatch, name, mutant):
+    monkeypatch.setattr(ob, name, mutant)
+    with pytest.raises(AssertionError):
+        _run_pins()
