@@ -1,0 +1,156 @@
+/*
+ * lutgemm.h -- C ABI of the MI355X (gfx950) BCQ LUT-GEMV library.
+ *
+ * The operation (LUT-GEMM, Park et al.; Elamur card "LUT-GEMM -- paper by
+ * Park et al. (2022)", section "Summary"; pith.science page of the same title,
+ * original abstract): y = W_hat * x for fp16 activations x and a weight matrix
+ * held in binary-coding quantization (BCQ),
+ *
+ *     W_hat[j][k] = sum_{i<q} alpha[i][j][k/g] * b_i[j][k]  (+ offset[j][k/g]),
+ *     b_i[j][k] in {-1, +1},
+ *
+ * computed without ever forming W_hat: for every 8-input chunk of x all 256
+ * signed sums are built once into a table, and each weight byte (the 8 sign
+ * bits of one plane, row and chunk) selects its sum, which is scaled by alpha
+ * and accumulated (card section "Interesting ideas: Lookup tables instead of
+ * multiplications"). Scales are group-wise with group size g (card section
+ * "Interesting ideas: Group size as a separate hyper-parameter"); the optional
+ * per-group offset lets a uniform int-q matrix be held exactly as BCQ (card
+ * section "Interesting ideas: One format for many schemes").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Plain pointers and sizes only; no C++ or framework types cross this ABI,
+ *   and no C++ exception escapes it. Every function returns a status code
+ *   (lutgemm_status) unless stated otherwise.
+ * - The caller owns every buffer, host and device. The library never
+ *   allocates, frees or synchronizes device memory or streams.
+ * - fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
+ * - Logical (unpacked) weight format, used as packer input:
+ *     bits   uint8  [q][N][K/8]  bit t (least significant first) of byte c of
+ *                                row j in plane i is the sign of weight
+ *                                (j, 8c+t): 1 means +1, 0 means -1;
+ *     alpha  fp16   [q][N][K/g]
+ *     offset fp16   [N][K/g]     (only when has_offset)
+ * - Packed (device) format, produced by bcq_pack / bcq_pack_uniform and read
+ *   by lutgemm_run. Rows are padded to Npad = 16*ceil(N/16) and 8-input
+ *   chunks to 64*ceil(K/512); padding bytes and scales are zero.
+ *     bits   byte   [Npad/16][ceil(K/512)][q][64][16]   (row tile, input tile,
+ *                                plane, chunk in tile, row in tile)
+ *     alpha  fp16   [Npad/16][K/g][q][16]
+ *     offset fp16   [Npad/16][K/g][16]
+ * - Shape rules (else LUTGEMM_ERR_SHAPE): N >= 0, K >= 0, K % 8 == 0,
+ *   1 <= q <= 8, g >= 8, g % 8 == 0, K % g == 0 (when K > 0),
+ *   has_offset in {0, 1}, N and K below 2^30, 0 <= m <= 65535.
+ */
+#ifndef LUTGEMM_H
+#define LUTGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LUTGEMM_ABI_VERSION 1
+
+typedef enum lutgemm_status {
+  LUTGEMM_OK = 0,
+  LUTGEMM_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  LUTGEMM_ERR_SHAPE = 2,       /* N, K, q, g, has_offset or m breaks the shape rules */
+  LUTGEMM_ERR_VALUE = 3,       /* code/zero-point >= 2^q, non-finite scale, alpha or */
+                               /* offset, or a rewritten scale that overflows fp16   */
+  LUTGEMM_ERR_BUFFER = 4,      /* an output buffer or the workspace is too small     */
+  LUTGEMM_ERR_ALIGN = 5,       /* a device pointer is not aligned as required        */
+  LUTGEMM_ERR_UNSUPPORTED = 6, /* the current device is not gfx950                   */
+  LUTGEMM_ERR_HIP = 7,         /* a HIP runtime call or a kernel launch failed       */
+  LUTGEMM_ERR_INTERNAL = 8     /* unexpected internal failure                        */
+} lutgemm_status;
+
+typedef struct lutgemm_shape {
+  int32_t N;          /* output rows                                 */
+  int32_t K;          /* inputs per row (reduction length)           */
+  int32_t q;          /* sign planes, 1..8                           */
+  int32_t g;          /* inputs per scale group                      */
+  int32_t has_offset; /* 1 if a per-(row, group) offset is present   */
+} lutgemm_shape;
+
+/* LUTGEMM_ABI_VERSION of the built library. Never fails. */
+int lutgemm_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* lutgemm_status_string(int status);
+
+/* Validate a shape against the shape rules. */
+int lutgemm_check_shape(const lutgemm_shape* s);
+
+/* Sizes of the packed format for shape *s: bytes of packed bits, and counts
+ * (fp16 elements) of packed alpha and packed offset (0 without offset).
+ * Any output pointer may be NULL. Host only; no HIP call. */
+int lutgemm_packed_sizes(const lutgemm_shape* s, size_t* bits_bytes,
+                         size_t* alpha_count, size_t* offset_count);
+
+/* Device workspace lutgemm_run needs for shape *s at batch m, in bytes (0 when
+ * none). The workspace holds split-reduction partial sums and, at its start,
+ * arrival counters. It must be zero-filled before its first use (for example
+ * with lutgemm_workspace_init); every call that completes leaves the counters
+ * zero again, so one workspace serves any later call of any shape whose
+ * requirement it meets. Host only; no HIP call. */
+int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes);
+
+/* Zero-fill `bytes` of device workspace asynchronously on `stream`
+ * (a hipStream_t, NULL for the default stream). */
+int lutgemm_workspace_init(void* d_workspace, size_t bytes, void* stream);
+
+/* Pack a BCQ matrix from the logical format into the device format.
+ * Host only (CPU), deterministic: the output bytes are fully determined by
+ * the inputs. `offset` must be non-NULL exactly when s->has_offset.
+ * Rejects non-finite alpha/offset values (LUTGEMM_ERR_VALUE) and output
+ * buffers smaller than lutgemm_packed_sizes (LUTGEMM_ERR_BUFFER). On error
+ * nothing has been written. */
+int bcq_pack(const lutgemm_shape* s, const uint8_t* bits, const uint16_t* alpha,
+             const uint16_t* offset, uint8_t* out_bits, size_t out_bits_bytes,
+             uint16_t* out_alpha, size_t out_alpha_count, uint16_t* out_offset,
+             size_t out_offset_count);
+
+/* Rewrite a uniform int-q matrix, W[j][k] = scale[j][k/g] * (codes[j][k] -
+ * zero[j][k/g]), as BCQ with q planes plus offset, and pack it (card sections
+ * "Summary" and "Interesting ideas: One format for many schemes").
+ *   codes uint8 [N][K] (< 2^q), scale fp16 [N][K/g], zero uint8 [N][K/g] (< 2^q).
+ * Plane i holds bit i of the code, alpha_i = scale * 2^(i-1) and
+ * offset = scale * ((2^q - 1)/2 - zero), each rounded to the nearest fp16
+ * (ties to even). s->has_offset must be 1. *n_rounded (may be NULL) receives
+ * the number of groups for which any of these values was not exactly
+ * representable in fp16. Host only; on error nothing has been written. */
+int bcq_pack_uniform(const lutgemm_shape* s, const uint8_t* codes,
+                     const uint16_t* scale, const uint8_t* zero,
+                     uint8_t* out_bits, size_t out_bits_bytes,
+                     uint16_t* out_alpha, size_t out_alpha_count,
+                     uint16_t* out_offset, size_t out_offset_count,
+                     size_t* n_rounded);
+
+/* y = W_hat x on the current HIP device, enqueued on `stream` (a hipStream_t;
+ * NULL for the default stream). Asynchronous: returns after the launch.
+ *   d_bits, d_alpha, d_offset: packed device format (d_offset only when
+ *       s->has_offset, else ignored);
+ *   d_x  fp16 [m][K] row-major;  d_y  fp16 [m][N] row-major, overwritten;
+ *   d_workspace: at least lutgemm_workspace_size bytes (may be NULL when that
+ *       size is 0); calls that overlap in time must not share a workspace.
+ * Alignment (else LUTGEMM_ERR_ALIGN): d_bits, d_x and d_workspace 16 bytes,
+ * d_alpha and d_offset 4 bytes, d_y 2 bytes.
+ * Arithmetic: table entries, scaling and accumulation in fp32; y rounded to
+ * fp16 to nearest-even. Results are bitwise reproducible for a fixed shape and
+ * batch. All argument checks run before any HIP call; on error nothing is
+ * launched. Faults inside the kernel surface at the caller's next
+ * synchronization of `stream`. */
+int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits,
+                const void* d_alpha, const void* d_offset, const void* d_x,
+                void* d_y, void* d_workspace, size_t workspace_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LUTGEMM_H */

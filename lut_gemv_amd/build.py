@@ -1,0 +1,77 @@
+"""Build the HIP library ``liblutgemm.so`` in-tree for gfx950.
+
+Usage: ``python -m lut_gemv_amd.build`` (or ``__graft_entry__.build()``).
+Host code (the packer) is compiled with g++, device code with hipcc, and the
+two are linked into one shared library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "liblutgemm.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
+CXX = os.environ.get("CXX", "g++")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-mcode-object-version=5",
+    # keep hipcc from emitting packed fp32 arithmetic
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}")
+    if verbose and r.stdout.strip():
+        print(r.stdout, flush=True)
+    return r.stdout
+
+
+def build(verbose: bool = False, extra_hip_flags=()) -> str:
+    """Compile every source and link ``liblutgemm.so``; returns its path."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    incs = [f"-I{INCLUDE}", f"-I{CSRC}"]
+    tmp = tempfile.mkdtemp(prefix="lutgemm_build_")
+    try:
+        pack_o = os.path.join(tmp, "pack.o")
+        kern_o = os.path.join(tmp, "lutgemv.o")
+        jobs = [
+            [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "pack.cpp"), "-o", pack_o],
+            [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c",
+             os.path.join(CSRC, "lutgemv.hip"), "-o", kern_o],
+        ]
+        with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+            for f in [ex.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        out_tmp = LIB_PATH + ".tmp"
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", pack_o, kern_o,
+              "-pthread", "-o", out_tmp], verbose)
+        os.replace(out_tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Acceptance per output (the tolerance the GEMV is specified to): |y_gpu - y_ref|
+<= 1e-3 * sum_k |W_hat[j,k] x[k]| + 1e-4. Small problems are checked on every
+output; the full-size workloads, run in the launch configuration the benchmark
+times, are checked on sampled rows the oracle computes one by one.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import lut_gemv_amd as lg  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _gpu_y(pw, x_np):
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(DEV)
+    y = pw(x)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _sample_rows(N, n, seed=0):
+    if N <= n:
+        return np.arange(N)
+    rng = np.random.default_rng(seed)
+    edge = np.r_[np.arange(min(32, N)), np.arange(max(0, N - 32), N)]
+    return np.unique(np.r_[edge, rng.choice(N, size=n, replace=False)])
+
+
+def _check(y_gpu, w, rows=None, ref=None):
+    if ref is None:
+        ref, bound = oracle.gemv(w.bits, w.alpha, w.offset, w.x, w.g, rows=rows)
+    else:
+        ref, bound = ref
+    yg = y_gpu if rows is None else y_gpu[:, rows]
+    ok, worst = oracle.parity_ok(yg.astype(np.float64), ref, bound)
+    _say(f"{w.name}: worst err/tol = {worst:.3f} over {yg.size} outputs")
+    assert ok, f"{w.name}: worst err/tol {worst}"
+    return worst
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    _say(f"device {torch.cuda.get_device_name(0)}")
+    assert lg.abi_version() == 1
+    yield
+
+
+# ---------------------------------------------------------------- named workloads
+
+def test_tiny_all_outputs():
+    w = workloads.generate("tiny")
+    _say("tiny 512x512 q3 g128")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    _check(_gpu_y(pw, w.x), w)
+
+
+def test_opt175b_ffn_up_sampled():
+    w = workloads.generate("opt175b_ffn_up")
+    _say("opt175b_ffn_up 49152x12288 q3 g128 m1")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    y = _gpu_y(pw, w.x)
+    assert np.isfinite(y).all()
+    _check(y, w, rows=_sample_rows(w.N, 2048))
+
+
+def test_llama7b_int4_uniform_all_outputs():
+    w = workloads.generate("llama7b_mlp_int4")
+    _say("llama7b_mlp_int4 11008x4096 int4 zero 8 -> BCQ q4 + offset")
+    pw = lg.PackedBCQ.from_uniform(w.codes, w.scale, w.zero, w.q, w.g)
+    y = _gpu_y(pw, w.x)
+    # against the uniform matrix by definition: s * (c - z)
+    Wd = oracle.dequant_uniform(w.codes, w.scale, w.zero, w.g)
+    x64 = w.x.astype(np.float64)
+    ref = x64 @ Wd.T
+    bound = np.abs(x64) @ np.abs(Wd).T
+    ok, worst = oracle.parity_ok(y.astype(np.float64), ref, bound)
+    _say(f"llama7b vs dequantized definition: worst {worst:.3f}; n_rounded={pw.n_rounded}")
+    assert ok
+    # and against the BCQ form the rewrite produced
+    bits, alpha, off, _ = oracle.uniform_to_bcq(w.codes, w.scale, w.zero, w.q, w.g)
+    wb = workloads.Workload(w.name, w.N, w.K, w.q, w.g, w.m, w.x, bits, alpha, off)
+    _check(y, wb, rows=_sample_rows(w.N, 1024))
+
+
+@pytest.mark.parametrize("m", [4, 16, 32])
+def test_decode_batch_sampled(m):
+    w = workloads.generate(f"decode_m{m}")
+    _say(f"decode m={m} 12288x12288 q3 g128")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    y = _gpu_y(pw, w.x)
+    _check(y, w, rows=_sample_rows(w.N, 512, seed=m))
+
+
+@pytest.mark.parametrize("q", [1, 2, 4])
+@pytest.mark.parametrize("g", [32, 64, 128, 8192])
+def test_subbit_sweep_sampled(q, g):
+    w = workloads.generate(f"subbit_q{q}_g{g}")
+    _say(f"subbit q={q} g={g} 28672x8192")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    y = _gpu_y(pw, w.x)
+    _check(y, w, rows=_sample_rows(w.N, 1024, seed=q * 1000 + g))
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("N,K,q,g,m,off", [
+    (1, 512, 3, 128, 1, False),       # one row
+    (17, 520, 3, 8, 1, True),         # ragged rows and a ragged 1-chunk input tile, g=8
+    (1000, 4104, 2, 24, 3, True),     # g not a multiple of 32; ragged everything
+    (64, 8, 1, 8, 2, False),          # K = 8: one chunk
+    (300, 1536, 5, 64, 5, True),      # q=5, batch not a multiple of 4
+    (129, 2048, 6, 256, 2, False),
+    (77, 1024, 7, 32, 1, True),
+    (48, 1024, 8, 16, 4, True),       # q=8, g=16
+    (4096, 512, 4, 512, 7, False),
+    (20000, 1024, 3, 128, 1, False),  # many row blocks, short K
+])
+def test_edge_shapes_all_outputs(N, K, q, g, m, off):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + K + q, with_offset=off, name=f"edge_{N}x{K}q{q}g{g}m{m}")
+    _say(f"edge N={N} K={K} q={q} g={g} m={m} offset={off}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    _check(_gpu_y(pw, w.x), w)
+
+
+def test_zero_input_gives_exact_zero():
+    w = workloads.random_bcq(256, 1024, 3, 128, m=2, seed=3, with_offset=True, x_dist="zeros")
+    _say("x = 0")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    y = _gpu_y(pw, w.x)
+    assert (y.view(np.uint16) & 0x7FFF == 0).all()
+
+
+def test_integer_case_is_exact():
+    """q=1, alpha=1, integer x: every partial sum is an integer below 2^11, so
+    the fp32 path and the fp16 output are exact: y = B x in integers."""
+    rng = np.random.default_rng(9)
+    N, K = 200, 1024
+    bits = rng.integers(0, 256, size=(1, N, K // 8), dtype=np.uint8)
+    alpha = np.ones((1, N, K // 128), np.float16)
+    xi = rng.integers(-1, 2, size=(1, K))
+    _say("integer exactness q=1")
+    pw = lg.PackedBCQ.from_bcq(bits, alpha, None, 128)
+    y = _gpu_y(pw, xi.astype(np.float16))
+    signs = oracle.signs(bits)[0].astype(np.int64)          # [N][K]
+    expect = xi @ signs.T
+    assert np.array_equal(y.astype(np.int64), expect)
+
+
+def test_unit_vector_probes():
+    """x = e_k returns column k of W_hat: probes the layout column by column."""
+    w = workloads.random_bcq(40, 1024, 3, 64, seed=4, with_offset=True)
+    Wh = oracle.reconstruct_rows(w.bits, w.alpha, w.offset, w.g, np.arange(w.N))
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    ks = [0, 1, 7, 8, 63, 64, 511, 512, 513, 1023]
+    X = np.zeros((len(ks), w.K), np.float16)
+    for r, k in enumerate(ks):
+        X[r, k] = 1
+    _say("unit-vector probes")
+    y = _gpu_y(pw, X)
+    for r, k in enumerate(ks):
+        col = Wh[:, k]
+        assert np.allclose(y[r].astype(np.float64), col, rtol=1e-3, atol=1e-4), k
+
+
+def test_empty_shapes():
+    _say("empty shapes")
+    w = workloads.random_bcq(32, 512, 2, 128, m=1, seed=1)
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    x0 = torch.zeros((0, 512), dtype=torch.float16, device=DEV)
+    assert pw(x0).shape == (0, 32)
+    # K = 0: the empty sum, y = 0
+    pk = lg.PackedBCQ(32, 0, 2, 8, torch.zeros(16, dtype=torch.uint8, device=DEV),
+                      torch.zeros(16, dtype=torch.int16, device=DEV))
+    y = torch.full((3, 32), 7.0, dtype=torch.float16, device=DEV)
+    pk(torch.zeros((3, 0), dtype=torch.float16, device=DEV), out=y)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+
+
+def test_bitwise_deterministic_and_split_consistent(monkeypatch):
+    w = workloads.random_bcq(4096, 8192, 3, 128, m=1, seed=5)
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    x = torch.from_numpy(w.x).to(DEV)
+    _say("determinism")
+    ys = [pw(x).clone() for _ in range(5)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+    # other splits of the reduction give results within tolerance of the oracle
+    for tile in ["4,1", "4,3", "2,16", "1,2"]:
+        monkeypatch.setenv("LUTGEMM_TILE", tile)
+        _say(f"split override {tile}")
+        y = pw(x)
+        torch.cuda.synchronize()
+        _check(y.cpu().numpy(), w, rows=_sample_rows(w.N, 512))
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves a large split call, then a smaller one, then the large again."""
+    big = workloads.random_bcq(8192, 12288, 3, 128, m=1, seed=6)
+    small = workloads.random_bcq(1024, 4096, 2, 64, m=3, seed=7)
+    pb = lg.PackedBCQ.from_bcq(big.bits, big.alpha, None, big.g)
+    ps = lg.PackedBCQ.from_bcq(small.bits, small.alpha, None, small.g)
+    ps._ws = pb.workspace(1)[0]        # share
+    _say("workspace reuse")
+    for w, p in [(big, pb), (small, ps), (big, pb), (small, ps)]:
+        y = _gpu_y(p, w.x)
+        _check(y, w, rows=_sample_rows(w.N, 256))
+
+
+def test_large_batch_and_many_rows():
+    w = workloads.random_bcq(64, 512, 2, 128, m=300, seed=8)
+    _say("m=300")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    _check(_gpu_y(pw, w.x), w)
+    w = workloads.random_bcq(200000, 512, 1, 512, m=1, seed=9)
+    _say("N=200000")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    _check(_gpu_y(pw, w.x), w, rows=_sample_rows(w.N, 2048))

@@ -1,0 +1,252 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared
+symbol, reports sizes, packs bit-exactly like the oracle, and rejects bad
+arguments before any HIP call. No GPU needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lut_gemv_amd as lg
+import oracle
+import workloads
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "lutgemm.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"bcq_pack", "bcq_pack_uniform", "lutgemm_run"} <= set(names)
+    L = lg.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # and the shared object's dynamic symbol table agrees
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", lg.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_abi_version_and_status_strings():
+    assert lg.abi_version() == 1
+    for st in range(9):
+        assert lg.status_string(st)
+    assert lg.status_string(123) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K,q,g,off", [(512, 512, 3, 128, False), (11008, 4096, 4, 128, True),
+                                         (17, 520, 3, 8, True), (1, 8, 1, 8, False),
+                                         (0, 512, 2, 64, False), (16, 0, 2, 8, True)])
+def test_sizes_match_oracle(N, K, q, g, off):
+    assert lg.packed_sizes(N, K, q, g, off) == oracle.packed_sizes(N, K, q, g, off)
+
+
+@pytest.mark.parametrize("args", [
+    (16, 12, 3, 8, 0),   # K % 8
+    (16, 512, 0, 128, 0), (16, 512, 9, 128, 0),   # q range
+    (16, 512, 3, 4, 0), (16, 512, 3, 12, 0),      # g >= 8, g % 8
+    (16, 520, 3, 128, 0),                         # K % g
+    (-1, 512, 3, 128, 0), (16, -8, 3, 8, 0),
+    (16, 512, 3, 128, 2),                         # has_offset
+    (1 << 30, 512, 3, 128, 0),
+])
+def test_shape_rules(args):
+    assert lg.lib().lutgemm_check_shape(ctypes.byref(lg.Shape(*args))) == 2
+
+
+def test_workspace_size_rules():
+    assert lg.workspace_size(512, 512, 3, 128, False, 0) == 0
+    assert lg.workspace_size(0, 512, 3, 128, False, 1) == 0
+    assert lg.workspace_size(16, 0, 3, 8, False, 1) == 0
+    with pytest.raises(lg.LutGemmError):
+        lg.workspace_size(512, 512, 3, 128, False, -1)
+    with pytest.raises(lg.LutGemmError):
+        lg.workspace_size(512, 512, 3, 128, False, 65536)
+    # a split reduction over the long input dimension needs a workspace
+    assert lg.workspace_size(49152, 12288, 3, 128, False, 1) > 0
+
+
+# ---------------------------------------------------------------- packing parity
+
+@pytest.mark.parametrize("N,K,q,g,off", [
+    (17, 520, 3, 8, True), (16, 512, 1, 512, False), (40, 1024, 4, 128, True),
+    (1, 8, 2, 8, False), (33, 1536, 8, 32, False), (100, 4096, 2, 4096, True),
+])
+def test_bcq_pack_bit_exact(N, K, q, g, off):
+    w = workloads.random_bcq(N, K, q, g, seed=N * 7 + q, with_offset=off)
+    pb, pa, po = lg.bcq_pack(w.bits, w.alpha, w.offset, g)
+    rb, ra, ro = oracle.pack(w.bits, w.alpha, w.offset, g)
+    assert np.array_equal(pb, rb)
+    assert np.array_equal(pa, ra)
+    if off:
+        assert np.array_equal(po, ro)
+    else:
+        assert po is None
+
+
+@pytest.mark.parametrize("name", ["tiny", "opt175b_ffn_up", "decode_m4", "subbit_q1_g32",
+                                  "subbit_q2_g8192", "subbit_q4_g64"])
+def test_bcq_pack_workloads_bit_exact(name):
+    w = workloads.generate(name)
+    pb, pa, _ = lg.bcq_pack(w.bits, w.alpha, None, w.g)
+    rb, ra, _ = oracle.pack(w.bits, w.alpha, None, w.g)
+    assert np.array_equal(pa, ra)
+    assert np.array_equal(pb, rb)
+
+
+def test_bcq_pack_uniform_llama_bit_exact():
+    w = workloads.generate("llama7b_mlp_int4")
+    pb, pa, po, n_r = lg.bcq_pack_uniform(w.codes, w.scale, w.zero, w.q, w.g)
+    bits, alpha, off, n_ref = oracle.uniform_to_bcq(w.codes, w.scale, w.zero, w.q, w.g)
+    rb, ra, ro = oracle.pack(bits, alpha, off, w.g)
+    assert n_r == n_ref
+    assert np.array_equal(pb, rb) and np.array_equal(pa, ra) and np.array_equal(po, ro)
+
+
+@pytest.mark.parametrize("q", [1, 2, 3, 5, 8])
+def test_bcq_pack_uniform_random_zero_points(q):
+    w = workloads.random_uniform(37, 256, q, 32, seed=q, zero=None)
+    pb, pa, po, n_r = lg.bcq_pack_uniform(w.codes, w.scale, w.zero, q, w.g)
+    bits, alpha, off, n_ref = oracle.uniform_to_bcq(w.codes, w.scale, w.zero, q, w.g)
+    rb, ra, ro = oracle.pack(bits, alpha, off, w.g)
+    assert n_r == n_ref
+    assert np.array_equal(pb, rb) and np.array_equal(pa, ra) and np.array_equal(po, ro)
+
+
+@pytest.mark.parametrize("z", [0, 1, 2, 3])
+def test_uniform_rounding_every_fp16_scale(z):
+    """Every finite fp16 scale (q=2: values s/2, s and s*(1.5 - z)) rounds like the oracle."""
+    pats = np.arange(0, 0x7C00, dtype=np.uint16)
+    s = pats.view(np.float16)
+    keep = np.abs(s.astype(np.float64) * max(1.0, abs(1.5 - z))) < 65504
+    s = s[keep]
+    N = s.size
+    codes = np.zeros((N, 8), np.uint8)
+    codes[:, 1] = 3
+    scale = s.reshape(N, 1)
+    zero = np.full((N, 1), z, np.uint8)
+    pb, pa, po, n_r = lg.bcq_pack_uniform(codes, scale, zero, 2, 8)
+    bits, alpha, off, n_ref = oracle.uniform_to_bcq(codes, scale, zero, 2, 8)
+    rb, ra, ro = oracle.pack(bits, alpha, off, 8)
+    assert n_r == n_ref
+    assert np.array_equal(pa, ra) and np.array_equal(po, ro) and np.array_equal(pb, rb)
+
+
+# ---------------------------------------------------------------- error paths
+
+def _pack_call(shape, bits, alpha, offset, nb, na, no):
+    ob = np.zeros(max(nb, 1), np.uint8)
+    oa = np.zeros(max(na, 1), np.uint16)
+    oo = np.zeros(max(no, 1), np.uint16)
+    p = lambda a: None if a is None else a.ctypes.data
+    return lg.lib().bcq_pack(ctypes.byref(shape), p(bits), p(alpha), p(offset), p(ob), nb,
+                             p(oa), na, p(oo), no)
+
+
+def test_bcq_pack_errors():
+    N, K, q, g = 16, 512, 2, 128
+    w = workloads.random_bcq(N, K, q, g, seed=1, with_offset=True)
+    nb, na, no = lg.packed_sizes(N, K, q, g, True)
+    s = lg.Shape(N, K, q, g, 1)
+    a16 = w.alpha.view(np.uint16).copy()
+    o16 = w.offset.view(np.uint16).copy()
+    assert _pack_call(s, w.bits, a16, o16, nb, na, no) == 0
+    assert _pack_call(s, w.bits, a16, None, nb, na, no) == 1            # offset missing
+    assert _pack_call(s, None, a16, o16, nb, na, no) == 1
+    assert _pack_call(s, w.bits, a16, o16, nb - 1, na, no) == 4         # buffer too small
+    assert _pack_call(s, w.bits, a16, o16, nb, na - 1, no) == 4
+    assert _pack_call(s, w.bits, a16, o16, nb, na, no - 1) == 4
+    bad = a16.copy()
+    bad[1, 3, 2] = 0x7C00                                               # +inf
+    assert _pack_call(s, w.bits, bad, o16, nb, na, no) == 3
+    bad[1, 3, 2] = 0x7E00                                               # NaN
+    assert _pack_call(s, w.bits, bad, o16, nb, na, no) == 3
+    bado = o16.copy()
+    bado[0, 0] = 0xFC00
+    assert _pack_call(s, w.bits, a16, bado, nb, na, no) == 3
+    assert _pack_call(lg.Shape(N, K, q, 100, 1), w.bits, a16, o16, nb, na, no) == 2
+    assert lg.lib().bcq_pack(None, None, None, None, None, 0, None, 0, None, 0) == 1
+
+
+def test_bcq_pack_uniform_errors():
+    w = workloads.random_uniform(16, 256, 4, 128, seed=0, zero=8)
+    with pytest.raises(lg.LutGemmError) as e:
+        lg.bcq_pack_uniform(w.codes | 16, w.scale, w.zero, 4, 128)
+    assert e.value.status == 3
+    with pytest.raises(lg.LutGemmError) as e:
+        lg.bcq_pack_uniform(w.codes, w.scale, w.zero + 8, 4, 128)
+    assert e.value.status == 3
+    sc = w.scale.copy()
+    sc[0, 0] = np.float16(np.inf)
+    with pytest.raises(lg.LutGemmError) as e:
+        lg.bcq_pack_uniform(w.codes, sc, w.zero, 4, 128)
+    assert e.value.status == 3
+    sc[0, 0] = np.float16(30000.0)      # 4 * s overflows fp16
+    with pytest.raises(lg.LutGemmError) as e:
+        lg.bcq_pack_uniform(w.codes, sc, w.zero, 4, 128)
+    assert e.value.status == 3
+    # has_offset must be 1 for the uniform rewrite
+    s = lg.Shape(16, 256, 4, 128, 0)
+    nb, na, no = lg.packed_sizes(16, 256, 4, 128, True)
+    ob, oa, oo = np.zeros(nb, np.uint8), np.zeros(na, np.uint16), np.zeros(no, np.uint16)
+    st = lg.lib().bcq_pack_uniform(ctypes.byref(s), w.codes.ctypes.data, w.scale.ctypes.data,
+                                   w.zero.ctypes.data, ob.ctypes.data, nb, oa.ctypes.data, na,
+                                   oo.ctypes.data, no, None)
+    assert st == 2
+
+
+def test_uniform_error_writes_nothing():
+    w = workloads.random_uniform(16, 256, 4, 128, seed=0, zero=8)
+    codes = w.codes.copy()
+    codes[-1, -1] = 200
+    nb, na, no = lg.packed_sizes(16, 256, 4, 128, True)
+    ob = np.full(nb, 0xAB, np.uint8)
+    oa = np.full(na, 0xABCD, np.uint16)
+    oo = np.full(no, 0xABCD, np.uint16)
+    s = lg.Shape(16, 256, 4, 128, 1)
+    st = lg.lib().bcq_pack_uniform(ctypes.byref(s), codes.ctypes.data, w.scale.ctypes.data,
+                                   w.zero.ctypes.data, ob.ctypes.data, nb, oa.ctypes.data, na,
+                                   oo.ctypes.data, no, None)
+    assert st == 3
+    assert (ob == 0xAB).all() and (oa == 0xABCD).all() and (oo == 0xABCD).all()
+
+
+def test_run_validates_before_any_hip_call():
+    """Every argument error is reported without touching the (absent) GPU."""
+    L = lg.lib()
+    ok = lg.Shape(64, 512, 3, 128, 0)
+    A = 0x100000     # fake, 16-byte aligned device addresses: never dereferenced
+    def run(shape, m, b=A, a=A, o=None, x=A, y=A, ws=None, wsb=0):
+        return L.lutgemm_run(ctypes.byref(shape) if shape is not None else None, m, b, a, o, x,
+                             y, ws, wsb, None)
+    assert run(None, 1) == 1
+    assert run(lg.Shape(64, 12, 3, 128, 0), 1) == 2
+    assert run(ok, -1) == 2
+    assert run(ok, 65536) == 2
+    assert run(ok, 0) == 0                       # empty batch: nothing to do
+    assert run(lg.Shape(0, 512, 3, 128, 0), 1) == 0
+    assert run(ok, 1, y=None) == 1
+    assert run(ok, 1, b=None) == 1
+    assert run(ok, 1, a=None) == 1
+    assert run(ok, 1, x=None) == 1
+    assert run(lg.Shape(64, 512, 3, 128, 1), 1, o=None) == 1
+    assert run(ok, 1, b=A + 8) == 5
+    assert run(ok, 1, x=A + 2) == 5
+    assert run(ok, 1, a=A + 2) == 5
+    assert run(ok, 1, y=A + 1) == 5
+    assert run(lg.Shape(64, 512, 3, 128, 1), 1, o=A + 2) == 5
+    big = lg.Shape(49152, 12288, 3, 128, 0)
+    need = lg.workspace_size(49152, 12288, 3, 128, False, 1)
+    assert need > 0
+    assert run(big, 1, ws=None, wsb=0) == 1
+    assert run(big, 1, ws=A, wsb=need - 1) == 4
+    assert run(big, 1, ws=A + 4, wsb=need) == 5
