@@ -92,16 +92,10 @@ int lutgemm_packed_sizes(const lutgemm_shape* s, size_t* bits_bytes,
                          size_t* alpha_count, size_t* offset_count);
 
 /* Device workspace lutgemm_run needs for shape *s at batch m, in bytes (0 when
- * none). The workspace holds split-reduction partial sums and, at its start,
- * arrival counters. It must be zero-filled before its first use (for example
- * with lutgemm_workspace_init); every call that completes leaves the counters
- * zero again, so one workspace serves any later call of any shape whose
- * requirement it meets. Host only; no HIP call. */
+ * none). It holds fp32 partial sums when the input dimension is split across
+ * workgroups; its contents need no initialisation and are scratch after the
+ * call. Host only; no HIP call. */
 int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes);
-
-/* Zero-fill `bytes` of device workspace asynchronously on `stream`
- * (a hipStream_t, NULL for the default stream). */
-int lutgemm_workspace_init(void* d_workspace, size_t bytes, void* stream);
 
 /* Pack a BCQ matrix from the logical format into the device format.
  * Host only (CPU), deterministic: the output bytes are fully determined by

@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "LutGemmError", "Shape", "lib", "abi_version", "status_string",
-    "check_shape", "packed_sizes", "workspace_size", "workspace_init",
+    "check_shape", "packed_sizes", "workspace_size",
     "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "PackedBCQ", "STATUS",
 ]
 
@@ -77,8 +77,6 @@ def lib() -> ctypes.CDLL:
     L.lutgemm_packed_sizes.argtypes = [_SHP, _SZP, _SZP, _SZP]
     L.lutgemm_workspace_size.restype = ctypes.c_int
     L.lutgemm_workspace_size.argtypes = [_SHP, ctypes.c_int32, _SZP]
-    L.lutgemm_workspace_init.restype = ctypes.c_int
-    L.lutgemm_workspace_init.argtypes = [_P, _SZ, _P]
     L.bcq_pack.restype = ctypes.c_int
     L.bcq_pack.argtypes = [_SHP, _P, _P, _P, _P, _SZ, _P, _SZ, _P, _SZ]
     L.bcq_pack_uniform.restype = ctypes.c_int
@@ -127,10 +125,6 @@ def workspace_size(N, K, q, g, has_offset, m) -> int:
     _check(lib().lutgemm_workspace_size(ctypes.byref(s), int(m), ctypes.byref(out)),
            "lutgemm_workspace_size")
     return out.value
-
-
-def workspace_init(d_workspace: int, nbytes: int, stream: int = 0):
-    _check(lib().lutgemm_workspace_init(d_workspace, nbytes, stream), "lutgemm_workspace_init")
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -240,13 +234,13 @@ class PackedBCQ:
         return obj
 
     def workspace(self, m: int):
-        """A zero-filled device workspace large enough for batch m (kept and reused)."""
+        """A device workspace large enough for batch m (kept and reused)."""
         import torch
         need = workspace_size(self.N, self.K, self.q, self.g, self.has_offset, m)
         if need == 0:
             return None, 0
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.d_bits.device)
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.d_bits.device)
         return self._ws, self._ws.numel()
 
     def __call__(self, x, out=None):
