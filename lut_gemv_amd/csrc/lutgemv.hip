@@ -9,20 +9,23 @@
 // expanded to fp16.
 //
 // Mapping onto CDNA4 (our design, not the pages'):
-//  * one workgroup of 8 wave64s per CU. Tables for one input tile (64 chunks =
-//    512 inputs) take 64 KiB of LDS: entry p of chunk t at word p*64 + t. Two
-//    such tables are kept (128 KiB) so the next step's table is built while the
-//    current one is read, with one barrier per step;
-//  * lane l of every wave always looks up chunk l, so the 64 lanes of a lookup
-//    hit 64 consecutive words modulo 256 B: no bank conflicts whatever the bytes;
-//  * a lane streams, per (row tile, plane), the 16 bytes of its chunk for 16 rows
-//    with one 128-bit buffer load; a wave reads 1 KiB contiguously. Each wave
-//    keeps the loads of the next two input tiles in flight (a ring of three
-//    register sets);
+//  * one persistent workgroup per CU (8 or 16 wave64s) walks a list of work
+//    items (row block, split of the input dimension, batch group). Tables for
+//    one input tile (64 chunks = 512 inputs) take 64 KiB of LDS: entry p of
+//    chunk t at word p*64 + t. Two such tables are kept (128 KiB), so the next
+//    step's table is built while the current one is read, with one barrier per
+//    step; the build walks each lane's entries in Gray-code order (one add per
+//    entry);
+//  * for the lookups a lane owns a 4-row x 4-chunk block of sign bytes (16
+//    bytes per plane, one 128-bit buffer load; a wave reads 1 KiB contiguously)
+//    and visits its chunks in a lane-rotated order, so the 64 lanes of every
+//    lookup read 64 different tables: no LDS bank conflicts whatever the bytes;
 //  * per lookup: one v_perm_b32 forms the LDS address from the weight byte, one
-//    ds_read_b32, one v_fma_mix_f32 (fp16 scale times fp32 entry into fp32);
-//  * group scales are fetched once per quad of lanes and broadcast inside the
-//    quad with DPP (a quad covers 32 inputs, inside one group when g % 32 == 0);
+//    ds_read_b32 and one add; when the block's four chunks share a scale group
+//    (g % 32 == 0) the four entries of a row are summed and scaled once with a
+//    v_fma_mix_f32 (fp16 scale times fp32 sum into an fp32 accumulator);
+//  * each wave keeps the loads of the next one or two input tiles in flight (a
+//    ring of register sets filled by unconditional buffer loads);
 //  * when the input dimension is split over workgroups to fill the CUs, each
 //    writes fp32 partial sums and a second kernel adds them in a fixed order:
 //    results are bitwise reproducible, and no cross-workgroup synchronisation
@@ -43,9 +46,6 @@ namespace lutgemm {
 namespace {
 
 constexpr int kLutWords = 256 * kChunkTile;   // one table tile: 64 KiB of fp32 entries
-constexpr int kWaves = 8;                     // waves per workgroup
-constexpr int kThreads = kWaves * 64;
-constexpr int kHiPerWave = 16 / kWaves;       // high nibbles of the pattern each wave builds
 constexpr int kCUs = 256;                     // MI355X compute units (dispatch heuristic)
 
 struct Params {
@@ -58,45 +58,13 @@ struct Params {
   int N, K, g, m;
   int C, KT, RT, G, S, Npad;
   int n_rb, n_bg, n_items;  // row blocks, batch groups, work items
+  int g_shift;              // log2(g) when g is a power of two, else -1
+  int g_span;               // most scale groups one input tile touches
 };
 
 __device__ __forceinline__ float h2f(uint32_t word, int hi) {
   const uint16_t bitsv = hi ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
   return (float)__builtin_bit_cast(_Float16, bitsv);
-}
-
-// Broadcast the value of lane u of each quad to the whole quad (DPP quad_perm).
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int u) {
-  switch (u) {
-    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, false);
-    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, false);
-    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, false);
-    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, false);
-  }
-}
-
-// Sum 16 per-lane values across the 64 lanes of a wave. Each step halves the
-// set a lane keeps and trades the other half with its partner, so the cost is
-// 8+4+2+1 exchanges instead of 16*6. On return lane l holds the total of row
-// l >> 2 (each row replicated in one quad). The summation order is fixed.
-__device__ __forceinline__ float reduce16(float (&v)[16], int lane) {
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int dist = 32 >> st;
-    const int half = 8 >> st;
-    const bool up = (lane & dist) != 0;
-#pragma unroll
-    for (int k = 0; k < half; ++k) {
-      const float vlo = v[k], vhi = v[k + half];   // select values, not addresses
-      const float send = up ? vlo : vhi;
-      const float keep = up ? vhi : vlo;
-      v[k] = keep + __shfl_xor(send, dist, 64);
-    }
-  }
-  float t = v[0];
-  t += __shfl_xor(t, 2, 64);
-  t += __shfl_xor(t, 1, 64);
-  return t;
 }
 
 // Raw buffer loads: an offset at or past num_records returns zero without a
@@ -118,122 +86,162 @@ __device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-// Where one work item's tiles are: item = (row block, split, batch group), with
-// the row block varying fastest. All fields are uniform over the workgroup.
-struct TileCtx {
-  int item, kt, kt1;      // input tile kt of the item's range [.., kt1)
-  int rt_first;           // first row tile of this wave in the item's row block
+// ------------------------------------------------------------------ work items
+// An item is (row block, split of the input tiles, batch group), row block
+// varying fastest. Its fields are uniform over the workgroup and are computed
+// once per item (the only integer divisions of the kernel).
+struct ItemCtx {
+  int item;               // item index (>= n_items: none)
+  int kt1;                // end of the item's input tiles
+  int rt_first;           // first row tile of this wave
   int valid_rpw;          // row tiles of this wave inside the matrix
   int r0, rows_here;      // batch rows of the item
   int split;
-  bool live;              // item exists (false: loads touch no memory)
 };
 
-__device__ __forceinline__ void item_range(const Params& p, int item, int* kt0, int* kt1) {
-  const int per = p.n_rb * p.S;
-  const int s = (item % per) / p.n_rb;
-  *kt0 = (int)((int64_t)s * p.KT / p.S);
-  *kt1 = (int)((int64_t)(s + 1) * p.KT / p.S);
-}
+// Position of one input tile in a workgroup's sequence of tiles.
+struct TilePos {
+  ItemCtx c;
+  int kt;
+  bool live;              // false past the workgroup's last item: loads touch no memory
+};
 
-template <int RPW, int MC>
-__device__ __forceinline__ TileCtx tile_ctx(const Params& p, int wave, int item, int kt, int kt1) {
-  TileCtx c;
-  c.item = item;
-  c.kt = kt;
-  c.kt1 = kt1;
-  c.live = item < p.n_items;
+template <int RPW, int MC, int W>
+__device__ __forceinline__ TilePos first_tile(const Params& p, int wave, int item) {
+  TilePos t;
+  t.c.item = item;
+  t.live = item < p.n_items;
   const int per = p.n_rb * p.S;
   const int bg = item / per;
   const int rem = item - bg * per;
-  c.split = rem / p.n_rb;
-  const int rb = rem - c.split * p.n_rb;
-  c.rt_first = (rb * kWaves + wave) * RPW;
-  c.valid_rpw = min(RPW, p.RT - c.rt_first);
-  c.r0 = bg * MC;
-  c.rows_here = c.live ? min(MC, p.m - c.r0) : 0;
-  return c;
+  t.c.split = rem / p.n_rb;
+  const int rb = rem - t.c.split * p.n_rb;
+  t.kt = t.c.split * p.KT / p.S;
+  t.c.kt1 = (t.c.split + 1) * p.KT / p.S;
+  t.c.rt_first = (rb * W + wave) * RPW;
+  t.c.valid_rpw = min(RPW, p.RT - t.c.rt_first);
+  t.c.r0 = bg * MC;
+  t.c.rows_here = t.live ? min(MC, p.m - t.c.r0) : 0;
+  return t;
 }
 
-// The tile after c in this workgroup's sequence: the next tile of the item, or
-// the first tile of the workgroup's next item (items advance by gridDim.x).
-template <int RPW, int MC>
-__device__ __forceinline__ TileCtx next_ctx(const Params& p, int wave, const TileCtx& c) {
-  if (c.kt + 1 < c.kt1) return tile_ctx<RPW, MC>(p, wave, c.item, c.kt + 1, c.kt1);
-  const int item = c.item + (int)gridDim.x;
-  int kt0, kt1;
-  item_range(p, item, &kt0, &kt1);
-  return tile_ctx<RPW, MC>(p, wave, item, kt0, kt1);
+// The tile after t: the next tile of the item, or the first tile of the
+// workgroup's next item (items advance by gridDim.x).
+template <int RPW, int MC, int W>
+__device__ __forceinline__ TilePos next_tile(const Params& p, int wave, const TilePos& t) {
+  if (t.kt + 1 < t.c.kt1) {
+    TilePos n = t;
+    n.kt = t.kt + 1;
+    return n;
+  }
+  return first_tile<RPW, MC, W>(p, wave, t.c.item + (int)gridDim.x);
+}
+
+// Lane roles. For the table build and the activations, lane l owns chunk l of
+// the input tile. For the lookups, lane l owns the lane block (r4, c4) of rows
+// 4*r4 .. +3 and chunks 4*c4 .. +3 (16 sign bytes per plane), with
+// r4 = bits 3-4 of l and c4 = bits 0-2 of l plus bit 5 of l as bit 3; it visits
+// its four chunks in the order b_k = (k + r4) & 3. At each of the four lookup
+// steps the 32 lanes of each half-wave then read 32 consecutive tables, one per
+// LDS bank, whatever the bytes are.
+struct LaneCtx {
+  int lane, wave, r4, c4;
+  uint32_t block;     // byte offset of this lane's block in a 1 KiB plane block
+  uint32_t tsel[4];   // (table index 4*c4 + b_k) * 4: byte 0 of the address
+  uint32_t psel[4];   // v_perm selector taking byte b_k of a sign word into byte 1
+};
+
+__device__ __forceinline__ LaneCtx lane_ctx() {
+  LaneCtx l;
+  l.lane = threadIdx.x & 63;
+  // wave index as a scalar: buffer descriptors built from it stay in SGPRs
+  l.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  l.r4 = (l.lane >> 3) & 3;
+  l.c4 = (l.lane & 7) | ((l.lane >> 5) << 3);
+  l.block = (uint32_t)(16 * l.r4 + l.c4) * 16u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b = (uint32_t)((k + l.r4) & 3);
+    l.tsel[k] = (4u * (uint32_t)l.c4 + b) << 2;
+    // byte 0 <- S1 byte 0 (table index), byte 1 <- S0 byte b (sign byte),
+    // byte 2 <- S1 byte 2 (table buffer), byte 3 <- 0
+    l.psel[k] = 0x0C020000u | ((4u + b) << 8);
+  }
+  return l;
 }
 
 // Everything one wave needs from memory for one input tile.
-template <int Q, int RPW, int MC, bool QUAD, bool OFF>
+// GQ: the four chunks of a lane block share one scale group (g % 32 == 0), so
+// scales (and offsets) are held per row; otherwise per row and visited chunk.
+template <int Q, int RPW, int MC, bool GQ, bool OFF>
 struct TileRegs {
-  static constexpr int AW = QUAD ? 2 * Q : 8 * Q;   // scale dwords per lane and row tile
-  static constexpr int OW = OFF ? (QUAD ? 2 : 8) : 0;
-  TileCtx c;
-  uint4 bw[RPW][Q];          // sign bytes: 16 rows of this lane's chunk, per plane
-  uint32_t aw[RPW][AW];      // fp16 scale pairs
+  static constexpr int AW = GQ ? 2 * Q : 8 * Q;   // scale dwords (fp16 pairs) per row tile
+  static constexpr int OW = OFF ? (GQ ? 2 : 8) : 0;
+  TilePos pos;
+  uint4 xv[MC];              // activations of chunk `lane`, per batch row
+  uint4 bw[RPW][Q];          // lane block per plane: word a = row 4*r4+a, byte b = chunk 4*c4+b
+  uint32_t aw[RPW][AW];      // GQ: [plane][row pair]; else [visit k][plane][row pair]
   uint32_t ow[RPW][OW > 0 ? OW : 1];
-  uint4 xv[MC];              // this lane's 8 activations, per batch row
 };
 
-struct LaneCtx {
-  int lane, wave, quad_lane;
-};
+__device__ __forceinline__ int group_of(const Params& p, int k) {
+  return p.g_shift >= 0 ? (k >> p.g_shift) : (k / p.g);
+}
 
-// Issue the loads of the tile described by T.c (all of them unconditional). A
-// dead item gives zero-length ranges: the instructions issue but touch no memory.
-template <int Q, int RPW, int MC, bool QUAD, bool OFF>
+// Issue the loads of the tile at T.pos (all of them unconditional; activations
+// first, so the table build waits only for those). A dead position gives
+// zero-length ranges: the instructions issue but touch no memory.
+template <int Q, int RPW, int MC, bool GQ, bool OFF>
 __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
-                                          TileRegs<Q, RPW, MC, QUAD, OFF>& T) {
-  using TR = TileRegs<Q, RPW, MC, QUAD, OFF>;
+                                          TileRegs<Q, RPW, MC, GQ, OFF>& T) {
   constexpr uint32_t kTileBytes = Q * kChunkTile * kRowTile;
-  const TileCtx& c = T.c;
-  const int kt = c.kt;
-  // activations first: the table build waits only for these
-  const int64_t k0 = (int64_t)kt * kChunkTile * 8;
-  const int64_t kin = c.live ? min((int64_t)kChunkTile * 8, (int64_t)p.K - k0) : 0;
+  const TilePos& t = T.pos;
+  const int k0 = t.kt * kChunkTile * 8;
+  const uint32_t kin = t.live ? (uint32_t)min(kChunkTile * 8, p.K - k0) : 0u;
 #pragma unroll
   for (int r = 0; r < MC; ++r) {
-    const uint32_t nb = (r < c.rows_here) ? (uint32_t)(kin * 2) : 0u;
-    const auto xr = make_rsrc(p.x + (size_t)(c.r0 + r) * p.K + k0, nb);
+    const uint32_t nb = (r < t.c.rows_here) ? kin * 2u : 0u;
+    const auto xr = make_rsrc(p.x + (size_t)(t.c.r0 + r) * p.K + k0, nb);
     T.xv[r] = load16(xr, (uint32_t)l.lane * 16u);
   }
-  // group of this lane's chunk, relative to the tile's first group
-  const int g_first = (int)(k0 / p.g);
-  int grp = (int)((k0 + l.lane * 8) / p.g);
-  grp = grp < p.G - 1 ? grp : p.G - 1;
-  const int g_rel = grp - g_first;
-  const int g_span = min(p.G - g_first, (kChunkTile * 8 + p.g - 1) / p.g + 1);
+  const int g_first = group_of(p, k0);
+  const uint32_t g_span = (uint32_t)min(p.G - g_first, p.g_span);
+  // group (relative to g_first) of each chunk this lane visits
+  uint32_t g_rel[GQ ? 1 : 4];
 #pragma unroll
-  for (int t = 0; t < RPW; ++t) {
-    const bool on = c.live && t < c.valid_rpw;
-    const size_t rt = (size_t)(c.rt_first + t);
-    const auto br = make_rsrc(p.bits + (rt * p.KT + kt) * kTileBytes, on ? kTileBytes : 0u);
+  for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+    const int chunk = 4 * l.c4 + (GQ ? 0 : ((k + l.r4) & 3));
+    int grp = group_of(p, k0 + 8 * chunk);
+    grp = grp < p.G - 1 ? grp : p.G - 1;
+    g_rel[k] = (uint32_t)(grp - g_first);
+  }
 #pragma unroll
-    for (int i = 0; i < Q; ++i)
-      T.bw[t][i] = load16(br, (uint32_t)(i * kChunkTile * kRowTile + l.lane * 16));
-    // scale block of (row tile, group): Q planes x 16 rows of fp16 = 8Q dwords
-    const auto ar = make_rsrc(p.alpha + (rt * p.G + g_first) * (8 * Q),
-                              on ? (uint32_t)(g_span * 32 * Q) : 0u);
-    const uint32_t abase =
-        (uint32_t)(g_rel * 32 * Q) + (QUAD ? (uint32_t)(l.quad_lane * 8 * Q) : 0u);
+  for (int i = 0; i < RPW; ++i) {
+    const bool on = t.live && i < t.c.valid_rpw;
+    const size_t rt = (size_t)(t.c.rt_first + i);
+    const auto br = make_rsrc(p.bits + (rt * p.KT + t.kt) * kTileBytes, on ? kTileBytes : 0u);
 #pragma unroll
-    for (int d = 0; d < TR::AW; d += 2) {
-      const uint2 v = load8(ar, abase + (uint32_t)d * 4u);
-      T.aw[t][d] = v.x;
-      T.aw[t][d + 1] = v.y;
+    for (int q = 0; q < Q; ++q)
+      T.bw[i][q] = load16(br, (uint32_t)(q * kChunkTile * kRowTile) + l.block);
+    // scale block of (row tile, group): [plane][16 rows] fp16; this lane's four
+    // rows of plane q are 8 bytes at q*32 + 8*r4
+    const auto ar = make_rsrc(p.alpha + (rt * p.G + g_first) * (8 * Q), on ? g_span * 32u * Q : 0u);
+#pragma unroll
+    for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint2 v = load8(ar, g_rel[k] * 32u * Q + (uint32_t)(q * 32 + 8 * l.r4));
+        T.aw[i][(k * Q + q) * 2] = v.x;
+        T.aw[i][(k * Q + q) * 2 + 1] = v.y;
+      }
     }
     if constexpr (OFF) {
-      const auto orr = make_rsrc(p.offset + (rt * p.G + g_first) * 8,
-                                 on ? (uint32_t)(g_span * 32) : 0u);
-      const uint32_t obase = (uint32_t)(g_rel * 32) + (QUAD ? (uint32_t)(l.quad_lane * 8) : 0u);
+      const auto orr = make_rsrc(p.offset + (rt * p.G + g_first) * 8, on ? g_span * 32u : 0u);
 #pragma unroll
-      for (int d = 0; d < TR::OW; d += 2) {
-        const uint2 v = load8(orr, obase + (uint32_t)d * 4u);
-        T.ow[t][d] = v.x;
-        T.ow[t][d + 1] = v.y;
+      for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+        const uint2 v = load8(orr, g_rel[k] * 32u + (uint32_t)(8 * l.r4));
+        T.ow[i][2 * k] = v.x;
+        T.ow[i][2 * k + 1] = v.y;
       }
     }
   }
@@ -244,180 +252,208 @@ __device__ __forceinline__ void unpack8(const uint4 xr, float (&x)[8]) {
   x[4] = h2f(xr.z, 0); x[5] = h2f(xr.z, 1); x[6] = h2f(xr.w, 0); x[7] = h2f(xr.w, 1);
 }
 
-// Table of lane l's chunk into buffer `buf`: the 256/kWaves entries whose high
-// nibble belongs to this wave. Entry p = sum_t (bit t of p ? +x_t : -x_t), as
-// ((+-x0 +-x1) + (+-x2 +-x3)) + ((+-x4 +-x5) + (+-x6 +-x7)) in fp32.
+// Table of lane l's chunk into buffer `buf`: the entries whose high nibble
+// belongs to this wave (16/W high nibbles with 16 waves, two with 8 or 12; with
+// 12 waves only the first 8 build). Entry p = sum_t (bit t of p ? +x_t : -x_t).
+// The entries are visited in Gray-code order of their varying bits, so each is
+// the previous one plus or minus 2 x_t (one add, sign known at compile time);
+// the first is summed directly.
+template <int W>
 __device__ __forceinline__ void build_table(float* lut, int buf, const LaneCtx& l, const uint4 xr) {
+  constexpr int HPW = W == 16 ? 1 : 2;        // high nibbles per building wave
+  constexpr int NB = HPW == 2 ? 5 : 4;        // pattern bits that vary within the wave
+  static_assert(W == 8 || W == 12 || W == 16, "8, 12 or 16 waves per workgroup");
+  if (W == 12 && l.wave >= 8) return;         // uniform over the wave
   float x[8];
   unpack8(xr, x);
-  const float a[4] = {-x[0] - x[1], x[0] - x[1], x[1] - x[0], x[0] + x[1]};
-  const float b[4] = {-x[2] - x[3], x[2] - x[3], x[3] - x[2], x[2] + x[3]};
-  float lo[16];
+  const int h0 = l.wave * HPW;                // first high nibble (even when HPW == 2)
+  const float c = ((h0 & 1) ? x[4] : -x[4]) + ((h0 & 2) ? x[5] : -x[5]);
+  const float d = ((h0 & 4) ? x[6] : -x[6]) + ((h0 & 8) ? x[7] : -x[7]);
+  float T = (-(x[0] + x[1]) - (x[2] + x[3])) + (c + d);   // pattern h0*16: low bits clear
+  float two[NB];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) lo[k] = a[k & 3] + b[k >> 2];
+  for (int t = 0; t < NB; ++t) two[t] = x[t] + x[t];       // bit 4 of the local pattern is x4
+  float* base = lut + buf * kLutWords + (h0 * 16) * kChunkTile + l.lane;
+  base[0] = T;
 #pragma unroll
-  for (int hh = 0; hh < kHiPerWave; ++hh) {
-    const int h = l.wave * kHiPerWave + hh;
-    const float c = ((h & 1) ? x[4] : -x[4]) + ((h & 2) ? x[5] : -x[5]);
-    const float d = ((h & 4) ? x[6] : -x[6]) + ((h & 8) ? x[7] : -x[7]);
-    const float hi = c + d;
-    float* dst = lut + buf * kLutWords + (h * 16) * kChunkTile + l.lane;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) dst[k * kChunkTile] = lo[k] + hi;
+  for (int n = 1; n < (1 << NB); ++n) {
+    const int t = __builtin_ctz(n);           // the bit that flips from gray(n-1) to gray(n)
+    const int pat = n ^ (n >> 1);
+    T += ((pat >> t) & 1) ? two[t] : -two[t];
+    base[pat * kChunkTile] = T;
   }
 }
 
-// Look up every row tile of batch row r in table buffer `buf`.
-template <int Q, int RPW, int MC, bool QUAD, bool OFF>
+__device__ __forceinline__ float lut_at(const float* lut, uint32_t byte_addr) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + byte_addr);
+}
+
+// Look up every row tile of batch row r in table buffer `buf`. Per plane and
+// row, a lane reads the entries its four sign bytes select; with GQ they are
+// summed and scaled once, else each is scaled by its chunk's group scale.
+template <int Q, int RPW, int MC, bool GQ, bool OFF>
 __device__ __forceinline__ void lookups(const LaneCtx& l, int r, int buf, const float* lut,
-                                        const TileRegs<Q, RPW, MC, QUAD, OFF>& T,
-                                        float (&acc)[MC][RPW][16]) {
-  // S1 operand of the address permute: byte 0 = lane * 4, byte 2 = table buffer
-  const uint32_t lane_sel = ((uint32_t)l.lane << 2) | ((uint32_t)buf << 16);
-  float csum = 0.f;
-  if constexpr (OFF) {   // sum of the chunk's 8 inputs (table entry 0xFF)
-    float x[8];
-    unpack8(T.xv[r], x);
-    csum = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+                                        const TileRegs<Q, RPW, MC, GQ, OFF>& T,
+                                        float (&acc)[MC][RPW][4]) {
+  const uint32_t bufbits = (uint32_t)buf << 16;
+  uint32_t tsel[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tsel[k] = l.tsel[k] | bufbits;
+  // offset term: entry 0xFF of a chunk's table is the sum of its 8 inputs
+  float csum[GQ ? 1 : 4];
+  if constexpr (OFF) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float e = lut_at(lut, (0xFFu << 8) | tsel[k]);
+      if constexpr (GQ) {
+        csum[0] = k == 0 ? e : csum[0] + e;
+      } else {
+        csum[k] = e;
+      }
+    }
   }
 #pragma unroll
-  for (int t = 0; t < RPW; ++t) {
-    if (t < T.c.valid_rpw) {  // uniform over the wave
+  for (int i = 0; i < RPW; ++i) {
+    if (i < T.pos.c.valid_rpw) {  // uniform over the wave
 #pragma unroll
-      for (int i = 0; i < Q; ++i) {
-        const uint32_t words[4] = {T.bw[t][i].x, T.bw[t][i].y, T.bw[t][i].z, T.bw[t][i].w};
+      for (int q = 0; q < Q; ++q) {
+        const uint32_t words[4] = {T.bw[i][q].x, T.bw[i][q].y, T.bw[i][q].z, T.bw[i][q].w};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          // byte address = buf * 64 KiB + byte(j) * 256 + lane * 4, one v_perm_b32:
-          // result byte 1 <- byte (j & 3) of the word; bytes 0, 2 <- lane_sel; byte 3 <- 0
-          const uint32_t sel = 0x0C020000u | ((4u + (uint32_t)(j & 3)) << 8);
-          const uint32_t addr = __builtin_amdgcn_perm(words[j >> 2], lane_sel, sel);
-          const float e = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + addr);
-          const int D = i * 8 + (j >> 1);     // scale dword index within the group block
-          uint32_t aword;
-          if constexpr (QUAD) {
-            aword = quad_bcast(T.aw[t][D % (2 * Q)], D / (2 * Q));
+        for (int a = 0; a < 4; ++a) {
+          if constexpr (GQ) {
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float e = lut_at(lut, __builtin_amdgcn_perm(words[a], tsel[k], l.psel[k]));
+              s = k == 0 ? e : s + e;
+            }
+            const uint32_t aword = T.aw[i][q * 2 + (a >> 1)];
+            acc[r][i][a] = __builtin_fmaf(h2f(aword, a & 1), s, acc[r][i][a]);
           } else {
-            aword = T.aw[t][D];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float e = lut_at(lut, __builtin_amdgcn_perm(words[a], tsel[k], l.psel[k]));
+              const uint32_t aword = T.aw[i][(k * Q + q) * 2 + (a >> 1)];
+              acc[r][i][a] = __builtin_fmaf(h2f(aword, a & 1), e, acc[r][i][a]);
+            }
           }
-          acc[r][t][j] = __builtin_fmaf(h2f(aword, j & 1), e, acc[r][t][j]);
         }
       }
       if constexpr (OFF) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int D = j >> 1;
-          uint32_t oword;
-          if constexpr (QUAD) {
-            oword = quad_bcast(T.ow[t][D % 2], D / 2);
-          } else {
-            oword = T.ow[t][D];
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+          for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+            const uint32_t oword = T.ow[i][2 * k + (a >> 1)];
+            acc[r][i][a] = __builtin_fmaf(h2f(oword, a & 1), csum[k], acc[r][i][a]);
           }
-          acc[r][t][j] = __builtin_fmaf(h2f(oword, j & 1), csum, acc[r][t][j]);
         }
       }
     }
   }
 }
 
-// Reduce the accumulators of a finished item across lanes, store them (fp16 y,
-// or this split's fp32 partials) and clear them for the next item.
+// Reduce the accumulators of a finished item over the 16 lanes that share a
+// row quad (lanes differing in bits 0-2 and 5), store them (fp16 y, or this
+// split's fp32 partials) and clear them. Each exchange halves the rows a lane
+// keeps; a lane ends with row 4*r4 + 2*bit5 + bit2 of its lane index. The
+// summation order is fixed.
 template <int RPW, int MC>
-__device__ __forceinline__ void finish_item(const Params& p, const LaneCtx& l, const TileCtx& c,
-                                            float (&acc)[MC][RPW][16]) {
+__device__ __forceinline__ void finish_item(const Params& p, const LaneCtx& l, const ItemCtx& c,
+                                            float (&acc)[MC][RPW][4]) {
   const bool split_mode = p.S > 1;
+  const bool up32 = (l.lane & 32) != 0, up4 = (l.lane & 4) != 0;
 #pragma unroll
   for (int r = 0; r < MC; ++r) {
 #pragma unroll
-    for (int t = 0; t < RPW; ++t) {
-      if (r < c.rows_here && t < c.valid_rpw) {
-        const float tot = reduce16(acc[r][t], l.lane);
-        const int row = (c.rt_first + t) * kRowTile + (l.lane >> 2);
-        if (l.quad_lane == 0) {
+    for (int i = 0; i < RPW; ++i) {
+      if (r < c.rows_here && i < c.valid_rpw) {
+        float v[4] = {acc[r][i][0], acc[r][i][1], acc[r][i][2], acc[r][i][3]};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float lo = v[k], hi = v[k + 2];
+          v[k] = (up32 ? hi : lo) + __shfl_xor(up32 ? lo : hi, 32, 64);
+        }
+        const float lo = v[0], hi = v[1];
+        float t = (up4 ? hi : lo) + __shfl_xor(up4 ? lo : hi, 4, 64);
+        t += __shfl_xor(t, 2, 64);
+        t += __shfl_xor(t, 1, 64);
+        const int row = (c.rt_first + i) * kRowTile + 4 * l.r4 + (up32 ? 2 : 0) + (up4 ? 1 : 0);
+        if ((l.lane & 3) == 0) {
           if (split_mode) {
-            p.partial[((size_t)c.split * p.m + (c.r0 + r)) * p.Npad + row] = tot;
+            p.partial[((size_t)c.split * p.m + (c.r0 + r)) * p.Npad + row] = t;
           } else if (row < p.N) {
-            p.y[(size_t)(c.r0 + r) * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)tot);
+            p.y[(size_t)(c.r0 + r) * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)t);
           }
         }
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[r][t][j] = 0.f;
+      for (int a = 0; a < 4; ++a) acc[r][i][a] = 0.f;
     }
   }
 }
 
-// All steps (one per batch row) of the tile in `cur`; `nxt` holds the next
-// tile (in flight) and `pre` receives the one after. Each step builds the next
-// step's table in the other buffer, reads its own, then waits at the step's
-// one barrier. A finished item is reduced and stored.
-template <int Q, int RPW, int MC, bool QUAD, bool OFF>
-__device__ __forceinline__ void tile_steps(const Params& p, const LaneCtx& l, float* lut, int& buf,
-                                           const TileRegs<Q, RPW, MC, QUAD, OFF>& cur,
-                                           const TileRegs<Q, RPW, MC, QUAD, OFF>& nxt,
-                                           TileRegs<Q, RPW, MC, QUAD, OFF>& pre,
-                                           float (&acc)[MC][RPW][16]) {
-  pre.c = next_ctx<RPW, MC>(p, l.wave, nxt.c);
-  load_tile(p, l, pre);
-#pragma unroll
-  for (int r = 0; r < MC; ++r) {
-    if (r < cur.c.rows_here) {  // uniform over the workgroup
-      if (r + 1 < cur.c.rows_here) {
-        build_table(lut, buf ^ 1, l, cur.xv[r + 1]);
-      } else if (nxt.c.live) {
-        build_table(lut, buf ^ 1, l, nxt.xv[0]);
-      }
-      lookups(l, r, buf, lut, cur, acc);
-      __syncthreads();
-      buf ^= 1;
-    }
-  }
-  if (cur.c.kt + 1 == cur.c.kt1) finish_item<RPW, MC>(p, l, cur.c, acc);
-}
-
-// Persistent kernel: workgroup b processes items b, b + gridDim.x, ... where an
-// item is (row block of kWaves*RPW row tiles, split of the input tiles, batch
-// group of MC rows). The three-tile load pipeline runs across item boundaries.
-// Q: sign planes; QUAD: scales shared by the 4 lanes of a quad (g % 32 == 0),
-// else every lane fetches the scales of its own group; OFF: offset term.
-template <int Q, int RPW, int MC, bool QUAD, bool OFF>
-__global__ void __launch_bounds__(kThreads, 2) lutgemv_kernel(Params p) {
+// Persistent kernel: workgroup b processes items b, b + gridDim.x, ... A ring
+// of NR register sets holds the tiles in flight: at the start of each tile the
+// loads of the tile NR-1 ahead are issued into the set the previous tile used.
+// Each step (one batch row of one tile) looks up its table, builds the next
+// step's table in the other LDS buffer, and ends at the step's one barrier.
+// Q: sign planes; RPW: row tiles per wave; MC: batch rows per item; GQ: see
+// TileRegs; OFF: offset term; W: waves per workgroup (8, 12 or 16).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR>
+__global__ void __launch_bounds__(W * 64, W / 4) lutgemv_kernel(Params p) {
   __shared__ float lut[2 * kLutWords];
+  using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
 
-  LaneCtx l;
-  l.lane = threadIdx.x & 63;
-  // wave index as a scalar: buffer descriptors built from it stay in SGPRs
-  l.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  l.quad_lane = l.lane & 3;
+  const LaneCtx l = lane_ctx();
 
-  float acc[MC][RPW][16];
+  float acc[MC][RPW][4];
 #pragma unroll
   for (int r = 0; r < MC; ++r)
 #pragma unroll
-    for (int t = 0; t < RPW; ++t)
+    for (int i = 0; i < RPW; ++i)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[r][t][j] = 0.f;
+      for (int a = 0; a < 4; ++a) acc[r][i][a] = 0.f;
 
-  TileRegs<Q, RPW, MC, QUAD, OFF> A, B, C;
-  {
-    int kt0, kt1;
-    item_range(p, blockIdx.x, &kt0, &kt1);
-    A.c = tile_ctx<RPW, MC>(p, l.wave, blockIdx.x, kt0, kt1);
+  TR R[NR];
+  R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
+  if (!R[0].pos.live) return;
+  load_tile(p, l, R[0]);
+#pragma unroll
+  for (int s = 1; s + 1 < NR; ++s) {
+    R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
+    load_tile(p, l, R[s]);
   }
-  if (!A.c.live) return;
-  load_tile(p, l, A);
-  B.c = next_ctx<RPW, MC>(p, l.wave, A.c);
-  load_tile(p, l, B);
   int buf = 0;
-  build_table(lut, 0, l, A.xv[0]);
+  build_table<W>(lut, 0, l, R[0].xv[0]);
   __syncthreads();
-  for (;;) {
-    tile_steps(p, l, lut, buf, A, B, C, acc);
-    if (!B.c.live) break;
-    tile_steps(p, l, lut, buf, B, C, A, acc);
-    if (!C.c.live) break;
-    tile_steps(p, l, lut, buf, C, A, B, acc);
-    if (!A.c.live) break;
+  bool done = false;
+  while (!done) {
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      if (!done) {
+        TR& cur = R[s];
+        TR& nxt = R[(s + 1) % NR];
+        TR& pre = R[(s + NR - 1) % NR];
+        pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
+        load_tile(p, l, pre);
+#pragma unroll
+        for (int r = 0; r < MC; ++r) {
+          if (r < cur.pos.c.rows_here) {  // uniform over the workgroup
+            lookups(l, r, buf, lut, cur, acc);
+            if (r + 1 < cur.pos.c.rows_here) {
+              build_table<W>(lut, buf ^ 1, l, cur.xv[r + 1]);
+            } else if (nxt.pos.live) {
+              build_table<W>(lut, buf ^ 1, l, nxt.xv[0]);
+            }
+            __syncthreads();
+            buf ^= 1;
+          }
+        }
+        if (cur.pos.kt + 1 == cur.pos.c.kt1) finish_item<RPW, MC>(p, l, cur.pos.c, acc);
+        done = !nxt.pos.live;
+      }
+    }
   }
 }
 
@@ -446,107 +482,149 @@ __global__ void zero_fill_kernel(uint16_t* y, size_t n) {
 
 using KernelFn = void (*)(Params);
 
-// Instances the dispatcher may choose; each keeps three tiles of sign bytes and
-// scales plus the accumulators within 256 VGPRs (two waves per SIMD).
-// (Scales fetched per lane, g % 32 != 0, run one batch row per workgroup.)
-template <int Q, int RPW, int MC, bool QUAD, bool OFF>
-constexpr bool kInstantiated =
-    (RPW == 1 && (MC == 1 || QUAD)) || (MC == 1 && RPW == 2 && (QUAD ? Q <= 4 : Q <= 2));
+// Register budget per wave: 256 VGPRs with 8 waves (two per SIMD), 128 with 16
+// (four per SIMD). An instance keeps a ring of NR tiles in flight, the
+// accumulators and some temporaries in that budget: three tiles when they fit,
+// else two (16 waves always use two).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int NR>
+constexpr int kVgprEstimate =
+    NR * (RPW * Q * 4 + RPW * (GQ ? 2 * Q : 8 * Q) + MC * 4 + (OFF ? RPW * (GQ ? 2 : 8) : 0)) +
+    4 * RPW * MC + 32;
 
-template <int Q, int RPW, int MC, bool QUAD, bool OFF>
+template <int W>
+constexpr int kBudget = W == 16 ? 128 : 256;
+
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
+constexpr int kRing =
+    (W == 8 && kVgprEstimate<Q, RPW, MC, GQ, OFF, 3> <= kBudget<W>) ? 3 : 2;
+
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
+constexpr bool kInstantiated =
+    (W == 16 ? (MC == 1 && GQ) : (W == 8)) &&
+    kVgprEstimate<Q, RPW, MC, GQ, OFF, kRing<Q, RPW, MC, GQ, OFF, W>> <= kBudget<W>;
+
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
 KernelFn kernel_or_null() {
-  if constexpr (kInstantiated<Q, RPW, MC, QUAD, OFF>) {
-    return lutgemv_kernel<Q, RPW, MC, QUAD, OFF>;
+  if constexpr (kInstantiated<Q, RPW, MC, GQ, OFF, W>) {
+    return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRing<Q, RPW, MC, GQ, OFF, W>>;
   } else {
     return nullptr;
   }
 }
 
-template <int Q, int RPW, int MC>
-KernelFn pick_flags(bool quad, bool off) {
-  if (quad) return off ? kernel_or_null<Q, RPW, MC, true, true>() : kernel_or_null<Q, RPW, MC, true, false>();
-  return off ? kernel_or_null<Q, RPW, MC, false, true>() : kernel_or_null<Q, RPW, MC, false, false>();
+template <int Q, int RPW, int MC, int W>
+KernelFn pick_flags(bool gq, bool off) {
+  if (gq)
+    return off ? kernel_or_null<Q, RPW, MC, true, true, W>() : kernel_or_null<Q, RPW, MC, true, false, W>();
+  return off ? kernel_or_null<Q, RPW, MC, false, true, W>() : kernel_or_null<Q, RPW, MC, false, false, W>();
 }
 
-template <int RPW, int MC>
-KernelFn pick_q(int q, bool quad, bool off) {
+template <int RPW, int MC, int W>
+KernelFn pick_q(int q, bool gq, bool off) {
   switch (q) {
-    case 1: return pick_flags<1, RPW, MC>(quad, off);
-    case 2: return pick_flags<2, RPW, MC>(quad, off);
-    case 3: return pick_flags<3, RPW, MC>(quad, off);
-    case 4: return pick_flags<4, RPW, MC>(quad, off);
-    case 5: return pick_flags<5, RPW, MC>(quad, off);
-    case 6: return pick_flags<6, RPW, MC>(quad, off);
-    case 7: return pick_flags<7, RPW, MC>(quad, off);
-    case 8: return pick_flags<8, RPW, MC>(quad, off);
+    case 1: return pick_flags<1, RPW, MC, W>(gq, off);
+    case 2: return pick_flags<2, RPW, MC, W>(gq, off);
+    case 3: return pick_flags<3, RPW, MC, W>(gq, off);
+    case 4: return pick_flags<4, RPW, MC, W>(gq, off);
+    case 5: return pick_flags<5, RPW, MC, W>(gq, off);
+    case 6: return pick_flags<6, RPW, MC, W>(gq, off);
+    case 7: return pick_flags<7, RPW, MC, W>(gq, off);
+    case 8: return pick_flags<8, RPW, MC, W>(gq, off);
     default: return nullptr;
   }
 }
 
-KernelFn pick_kernel(int q, int rpw, int mc, bool quad, bool off) {
+template <int W>
+KernelFn pick_rpw_mc(int q, int rpw, int mc, bool gq, bool off) {
   if (mc == 1) {
-    if (rpw == 2) return pick_q<2, 1>(q, quad, off);
-    if (rpw == 1) return pick_q<1, 1>(q, quad, off);
+    if (rpw == 2) return pick_q<2, 1, W>(q, gq, off);
+    if (rpw == 1) return pick_q<1, 1, W>(q, gq, off);
   } else if (mc == 2) {
-    if (rpw == 1) return pick_q<1, 2>(q, quad, off);
+    if (rpw == 2) return pick_q<2, 2, W>(q, gq, off);
+    if (rpw == 1) return pick_q<1, 2, W>(q, gq, off);
   } else if (mc == 4) {
-    if (rpw == 1) return pick_q<1, 4>(q, quad, off);
+    if (rpw == 2) return pick_q<2, 4, W>(q, gq, off);
+    if (rpw == 1) return pick_q<1, 4, W>(q, gq, off);
   }
   return nullptr;
 }
 
+KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w) {
+  if (w == 16) return pick_rpw_mc<16>(q, rpw, mc, gq, off);
+  if (w == 8) return pick_rpw_mc<8>(q, rpw, mc, gq, off);
+  return nullptr;
+}
+
 struct Config {
-  int RPW, MC, S;
+  int RPW, MC, S, W;
   int64_t n_rb, n_bg;
-  bool quad;
+  bool gq;
   size_t ws_bytes;
 };
 
-// Optional tuning override "RPW,S" (LUTGEMM_TILE); never needed for correctness.
-bool tile_override(int* rpw, int* s) {
+// Optional tuning override "RPW,S[,W[,MC]]" (LUTGEMM_TILE); never needed for correctness.
+bool tile_override(int* rpw, int* s, int* w, int* mc) {
   const char* e = getenv("LUTGEMM_TILE");
   if (!e || !*e) return false;
-  int a = 0, b = 0;
-  if (sscanf(e, "%d,%d", &a, &b) != 2) return false;
+  int a = 0, b = 0, c = 0, d = 0;
+  const int n = sscanf(e, "%d,%d,%d,%d", &a, &b, &c, &d);
+  if (n < 2) return false;
   *rpw = a;
   *s = b;
+  *w = n >= 3 ? c : 0;
+  *mc = n >= 4 ? d : 0;
   return true;
 }
 
-// Pick rows per wave and the split of the input tiles. The kernel is
-// persistent (one workgroup per CU, LDS-bound), so each CU works through
-// ceil(items / kCUs) items; the estimate charges that many items the tiles
-// they stream (weighted by row tiles per wave and batch rows) plus a reduction
-// cost per item, and a small cost for the extra reduction kernel.
+// Pick waves, rows per wave, batch rows per item and the split of the input
+// tiles. The kernel is persistent (one workgroup per CU, LDS-bound), so each
+// CU works through ceil(items / kCUs) items. The estimate charges each item
+// its tiles, weighted by the row tiles it covers and its batch rows (a tile
+// step of 16 row tiles is one unit; 8-wave instances pay for their lower
+// latency hiding), plus a small cost per item and one for the extra
+// reduction kernel a split needs.
 Config choose_config(const Geometry& G, int64_t m) {
   Config c{};
-  c.quad = (G.g % 32) == 0;
-  c.MC = !c.quad ? 1 : (m >= 4 ? 4 : (m >= 2 ? 2 : 1));
-  c.n_bg = (m + c.MC - 1) / c.MC;
+  c.gq = (G.g % 32) == 0;
+  c.W = 0;   // stays 0 if no instance fits (reported as an internal error)
   double best = 1e300;
-  for (int rpw : {2, 1}) {
-    if (!pick_kernel((int)G.q, rpw, c.MC, c.quad, G.has_offset)) continue;
-    const int64_t n_rb = (G.RT + kWaves * rpw - 1) / (kWaves * rpw);
+  struct Cand { int w, rpw, mc; double eff; };
+  const Cand cands[] = {{16, 2, 1, 1.0}, {16, 1, 1, 1.0}, {8, 2, 4, 1.3}, {8, 1, 4, 1.3},
+                        {8, 2, 2, 1.3}, {8, 1, 2, 1.3}, {8, 2, 1, 1.3}, {8, 1, 1, 1.3}};
+  for (const Cand& v : cands) {
+    if (v.mc > 1 && m < v.mc) continue;
+    if (!pick_kernel((int)G.q, v.rpw, v.mc, c.gq, G.has_offset, v.w)) continue;
+    const int64_t rows = (int64_t)v.w * v.rpw;            // row tiles per item
+    const int64_t n_rb = (G.RT + rows - 1) / rows;
+    const int64_t n_bg = (m + v.mc - 1) / v.mc;
     const int64_t smax = G.KT < 64 ? G.KT : 64;
     for (int64_t s = 1; s <= smax; ++s) {
-      const int64_t items = n_rb * c.n_bg * s;
+      const int64_t items = n_rb * n_bg * s;
       const int64_t per_cu = (items + kCUs - 1) / kCUs;
       const int64_t tiles = (G.KT + s - 1) / s;
-      const double cost = (double)per_cu * ((double)rpw * tiles * c.MC + 0.5 * rpw * c.MC) +
-                          (s > 1 ? 1.0 : 0.0) - 0.01 * rpw;
-      if (cost < best) {
+      const double unit = v.eff * (double)rows * v.mc / 16.0;
+      const double cost = (double)per_cu * (tiles * unit + 0.3 * unit) + (s > 1 ? 2.0 : 0.0);
+      if (cost < best - 1e-9) {
         best = cost;
-        c.RPW = rpw;
+        c.W = v.w;
+        c.RPW = v.rpw;
+        c.MC = v.mc;
         c.n_rb = n_rb;
+        c.n_bg = n_bg;
         c.S = (int)s;
       }
     }
   }
-  int orpw = 0, os = 0;
-  if (tile_override(&orpw, &os)) {
-    if ((orpw == 1 || orpw == 2) && pick_kernel((int)G.q, orpw, c.MC, c.quad, G.has_offset)) {
+  int orpw = 0, os = 0, ow = 0, omc = 0;
+  if (tile_override(&orpw, &os, &ow, &omc)) {
+    const int w = ow ? ow : c.W;
+    const int mc = omc ? omc : c.MC;
+    if (pick_kernel((int)G.q, orpw, mc, c.gq, G.has_offset, w)) {
+      c.W = w;
       c.RPW = orpw;
-      c.n_rb = (G.RT + kWaves * c.RPW - 1) / (kWaves * c.RPW);
+      c.MC = mc;
+      c.n_rb = (G.RT + (int64_t)c.W * c.RPW - 1) / ((int64_t)c.W * c.RPW);
+      c.n_bg = (m + c.MC - 1) / c.MC;
     }
     if (os >= 1) c.S = (int)(os < G.KT ? os : (G.KT > 0 ? G.KT : 1));
   }
@@ -587,7 +665,9 @@ int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes) {
   Geometry G = geometry(s);
   *bytes = 0;
   if (m == 0 || G.N == 0 || G.K == 0) return LUTGEMM_OK;
-  *bytes = choose_config(G, m).ws_bytes;
+  const Config c = choose_config(G, m);
+  if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
+  *bytes = c.ws_bytes;
   return LUTGEMM_OK;
 }
 
@@ -609,6 +689,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
           (G.has_offset && !aligned(d_offset, 4)))
         return LUTGEMM_ERR_ALIGN;
       c = choose_config(G, m);
+      if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
       if (c.ws_bytes) {
         if (!d_workspace) return LUTGEMM_ERR_NULL;
         if (workspace_bytes < c.ws_bytes) return LUTGEMM_ERR_BUFFER;
@@ -627,7 +708,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
       return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
     }
 
-    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.quad, G.has_offset);
+    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W);
     if (!fn) return LUTGEMM_ERR_INTERNAL;
     Params p{};
     p.bits = (const uint8_t*)d_bits;
@@ -647,13 +728,17 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     p.S = c.S;
     p.Npad = (int)G.Npad;
     p.n_rb = (int)c.n_rb;
+    p.g_shift = -1;
+    for (int b = 3; b < 31; ++b)
+      if (((int64_t)1 << b) == G.g) p.g_shift = b;
+    p.g_span = (int)((kChunkTile * 8 + G.g - 1) / G.g + 1);
     p.n_bg = (int)c.n_bg;
     const int64_t items = c.n_rb * c.n_bg * c.S;
     if (items > 0x7FFFFFFF - kCUs) return LUTGEMM_ERR_SHAPE;
     p.n_items = (int)items;
     dim3 grid((unsigned)(items < kCUs ? items : kCUs));
     void* args[] = {&p};
-    if (hipLaunchKernel((const void*)fn, grid, dim3(kThreads), args, 0, strm) != hipSuccess)
+    if (hipLaunchKernel((const void*)fn, grid, dim3(64 * c.W), args, 0, strm) != hipSuccess)
       return LUTGEMM_ERR_HIP;
     if (c.S > 1) {
       const size_t n = (size_t)m * G.N;

@@ -92,8 +92,14 @@ int check_outputs(const Geometry& G, uint8_t* ob, size_t obn, uint16_t* oa, size
   return LUTGEMM_OK;
 }
 
-// Scatter logical sign bytes bits[i][j][c] into the packed order
-// [rt][kt][i][c % 64][j % 16]; padding stays zero.
+// Offset of (row r, chunk c) inside one 1024-byte (row tile, input tile, plane)
+// block: 64 lane blocks of 16 bytes, lane block 16*(r/4) + c/4 holding rows
+// r/4*4 .. +3 and chunks c/4*4 .. +3 at byte 4*(r%4) + c%4.
+inline int64_t in_block(int64_t r, int64_t c) {
+  return ((r >> 2) * 16 + (c >> 2)) * 16 + (r & 3) * 4 + (c & 3);
+}
+
+// Scatter logical sign bytes bits[i][j][c] into the packed order; padding stays zero.
 void pack_bits(const Geometry& G, const uint8_t* bits, uint8_t* out) {
   const int64_t tile = (int64_t)kChunkTile * kRowTile;
   parallel_for(G.RT, [&](int64_t rt0, int64_t rt1) {
@@ -107,7 +113,7 @@ void pack_bits(const Geometry& G, const uint8_t* bits, uint8_t* out) {
           const uint8_t* src = bits + ((size_t)i * G.N + j) * G.C;
           for (int64_t c = 0; c < G.C; ++c) {
             const int64_t kt = c / kChunkTile, cl = c % kChunkTile;
-            base[((kt * G.q + i) * kChunkTile + cl) * kRowTile + r] = src[c];
+            base[(kt * G.q + i) * kChunkTile * kRowTile + in_block(r, cl)] = src[c];
           }
         }
       }
@@ -254,7 +260,7 @@ int bcq_pack_uniform(const lutgemm_shape* s, const uint8_t* codes, const uint16_
               for (int64_t i = 0; i < G.q; ++i) {
                 unsigned byte = 0;
                 for (int t = 0; t < 8; ++t) byte |= ((row[8 * c + t] >> i) & 1u) << t;
-                base[((kt * G.q + i) * kChunkTile + cl) * kRowTile + r] = (uint8_t)byte;
+                base[(kt * G.q + i) * kChunkTile * kRowTile + in_block(r, cl)] = (uint8_t)byte;
               }
             }
           }

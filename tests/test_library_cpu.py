@@ -71,8 +71,19 @@ def test_workspace_size_rules():
         lg.workspace_size(512, 512, 3, 128, False, -1)
     with pytest.raises(lg.LutGemmError):
         lg.workspace_size(512, 512, 3, 128, False, 65536)
-    # a split reduction over the long input dimension needs a workspace
-    assert lg.workspace_size(49152, 12288, 3, 128, False, 1) > 0
+    # few rows and a long input dimension: the reduction is split, which needs a workspace
+    assert lg.workspace_size(256, 65536, 3, 128, False, 1) > 0
+
+
+@pytest.mark.parametrize("q", range(1, 9))
+@pytest.mark.parametrize("g", [8, 16, 24, 32, 128, 4096])
+def test_every_configuration_has_a_kernel(q, g):
+    """The dispatcher finds a kernel instance for every plane count, group
+    class, offset flag and batch size (the workspace query reports it)."""
+    for off in (False, True):
+        for m in (1, 2, 3, 4, 5, 17, 64):
+            for N in (16, 4096):
+                lg.workspace_size(N, 4096 if 4096 % g == 0 else 24 * g, q, g, off, m)
 
 
 # ---------------------------------------------------------------- packing parity
@@ -244,8 +255,8 @@ def test_run_validates_before_any_hip_call():
     assert run(ok, 1, a=A + 2) == 5
     assert run(ok, 1, y=A + 1) == 5
     assert run(lg.Shape(64, 512, 3, 128, 1), 1, o=A + 2) == 5
-    big = lg.Shape(49152, 12288, 3, 128, 0)
-    need = lg.workspace_size(49152, 12288, 3, 128, False, 1)
+    big = lg.Shape(256, 65536, 3, 128, 0)
+    need = lg.workspace_size(256, 65536, 3, 128, False, 1)
     assert need > 0
     assert run(big, 1, ws=None, wsb=0) == 1
     assert run(big, 1, ws=A, wsb=need - 1) == 4

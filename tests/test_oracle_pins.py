@@ -280,16 +280,35 @@ def test_uniform_rewrite_rejects():
 
 # ---------------------------------------------------------------- packed layout
 
-def _unpack_by_reshape(pb, pa, po, q, N, K, g):
-    """Inverse of the packed layout written with reshapes/transposes (not loops)."""
+def _unpack_by_loops(pb, pa, po, q, N, K, g):
+    """Inverse of the packed layout, byte by byte from its definition (independent
+    of the reshapes inside the oracle's packer). Returns the logical arrays over
+    the padded extent."""
     RT = -(-N // 16)
     C = K // 8
     KT = -(-C // 64)
     G = K // g
-    b = pb.reshape(RT, KT, q, 64, 16).transpose(2, 0, 4, 1, 3).reshape(q, RT * 16, KT * 64)
-    a = pa.reshape(RT, G, q, 16).transpose(2, 0, 3, 1).reshape(q, RT * 16, G)
-    o = po.reshape(RT, G, 16).transpose(0, 2, 1).reshape(RT * 16, G) if po.size else None
-    return b[:, :N, :C], b, a[:, :N, :], a, (o[:N] if o is not None else None), o
+    b = np.zeros((q, RT * 16, KT * 64), np.uint8)
+    for rt in range(RT):
+        for kt in range(KT):
+            for i in range(q):
+                base = ((rt * KT + kt) * q + i) * 1024
+                for lane in range(64):
+                    r4, c4 = lane // 16, lane % 16
+                    for a in range(4):
+                        for bb in range(4):
+                            b[i, 16 * rt + 4 * r4 + a, 64 * kt + 4 * c4 + bb] = pb[base + lane * 16 + 4 * a + bb]
+    a_out = np.zeros((q, RT * 16, G), np.uint16)
+    o_out = np.zeros((RT * 16, G), np.uint16) if po.size else None
+    for rt in range(RT):
+        for grp in range(G):
+            for i in range(q):
+                for r in range(16):
+                    a_out[i, 16 * rt + r, grp] = pa[((rt * G + grp) * q + i) * 16 + r]
+            if o_out is not None:
+                for r in range(16):
+                    o_out[16 * rt + r, grp] = po[(rt * G + grp) * 16 + r]
+    return b, a_out, o_out
 
 
 @pytest.mark.parametrize("N,K,q,g,off", [(17, 520, 3, 8, True), (16, 512, 1, 512, False),
@@ -302,33 +321,41 @@ def test_pack_roundtrip(N, K, q, g, off):
     pb, pa, po = ob.pack(bits, alpha, offset, g)
     nb, na, no = ob.packed_sizes(N, K, q, g, off)
     assert pb.size == nb and pa.size == na and po.size == no
-    b, b_full, a, a_full, o, o_full = _unpack_by_reshape(pb, pa, po, q, N, K, g)
-    assert np.array_equal(b, bits)
-    assert np.array_equal(a, alpha.view(np.uint16))
+    b_full, a_full, o_full = _unpack_by_loops(pb, pa, po, q, N, K, g)
+    assert np.array_equal(b_full[:, :N, :K // 8], bits)
+    assert np.array_equal(a_full[:, :N, :], alpha.view(np.uint16))
     # padding is zero
     assert not b_full[:, N:, :].any() and not b_full[:, :, K // 8:].any()
     assert not a_full[:, N:, :].any()
     if off:
-        assert np.array_equal(o, offset.view(np.uint16))
+        assert np.array_equal(o_full[:N], offset.view(np.uint16))
         assert not o_full[N:].any()
 
 
 def test_pack_single_bit_positions():
-    """Hand-placed bytes land where the layout definition says."""
+    """Hand-placed bytes land where the layout definition says: block
+    ((rt*KT + kt)*q + i)*1024, lane block 16*(16*r4 + c4), byte 4*a + b for
+    row 16 rt + 4 r4 + a and chunk 64 kt + 4 c4 + b."""
     q, N, K, g = 2, 20, 1024, 256
     bits = np.zeros((q, N, K // 8), np.uint8)
-    # (plane, row, chunk) -> expected flat index: ((rt*KT + kt)*q + i)*1024 + c*16 + r
-    cases = {(1, 17, 70): ((1 * 2 + 1) * 2 + 1) * 1024 + 6 * 16 + 1,
-             (0, 0, 0): 0,
-             (0, 15, 63): 63 * 16 + 15,
-             (1, 3, 127): ((0 * 2 + 1) * 2 + 1) * 1024 + 63 * 16 + 3}
+    cases = {
+        # (plane, row, chunk): row 17 -> rt 1, r4 0, a 1; chunk 70 -> kt 1, c4 1, b 2
+        (1, 17, 70): ((1 * 2 + 1) * 2 + 1) * 1024 + 16 * (16 * 0 + 1) + 4 * 1 + 2,
+        (0, 0, 0): 0,
+        # row 15 -> rt 0, r4 3, a 3; chunk 63 -> kt 0, c4 15, b 3
+        (0, 15, 63): 16 * (16 * 3 + 15) + 4 * 3 + 3,
+        # row 3 -> r4 0, a 3; chunk 127 -> kt 1, c4 15, b 3
+        (1, 3, 127): ((0 * 2 + 1) * 2 + 1) * 1024 + 16 * 15 + 4 * 3 + 3,
+        # row 6 -> r4 1, a 2; chunk 9 -> kt 0, c4 2, b 1
+        (0, 6, 9): 16 * (16 * 1 + 2) + 4 * 2 + 1,
+    }
     for n, (i, j, c) in enumerate(cases):
         bits[i, j, c] = n + 1
     alpha = np.zeros((q, N, K // g), np.float16)
     alpha[1, 18, 3] = 1.0          # rt 1, grp 3, plane 1, row 2 -> ((1*4+3)*2+1)*16 + 2
     pb, pa, _ = ob.pack(bits, alpha, None, g)
     for n, (key, idx) in enumerate(cases.items()):
-        assert pb[idx] == n + 1
+        assert pb[idx] == n + 1, key
     assert np.count_nonzero(pb) == len(cases)
     assert pa[((1 * 4 + 3) * 2 + 1) * 16 + 2] == np.float16(1.0).view(np.uint16)
     assert np.count_nonzero(pa) == 1
@@ -430,7 +457,7 @@ def _mut_pack_rows_chunks_swapped(bits, alpha, offset, g):
     pb, pa, po = _orig_pack(bits, alpha, offset, g)
     q, N, C = bits.shape
     RT, KT = -(-N // 16), -(-C // 64)
-    pb = pb.reshape(RT, KT, q, 64, 16).transpose(0, 1, 2, 4, 3).reshape(-1).copy()
+    pb = pb.reshape(RT, KT, q, 4, 16, 4, 4).transpose(0, 1, 2, 3, 4, 6, 5).reshape(-1).copy()
     return pb, pa, po
 
 
