@@ -94,10 +94,17 @@ int lutgemm_packed_sizes(const lutgemm_shape* s, size_t* bits_bytes,
                          size_t* alpha_count, size_t* offset_count);
 
 /* Device workspace lutgemm_run needs for shape *s at batch m, in bytes (0 when
- * none). It holds fp32 partial sums when the input dimension is split across
- * workgroups; its contents need no initialisation and are scratch after the
- * call. Host only; no HIP call. */
+ * none). It is needed when the input dimension is split across workgroups:
+ * it holds arrival counters (at its start) and fp32 partial sums. It must be
+ * zero-filled before its first use (lutgemm_workspace_init); every call that
+ * completes leaves the counters zero again, so one workspace then serves any
+ * later call whose requirement it meets. Host only; no HIP call. */
 int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes);
+
+/* Zero-fill `bytes` of device workspace on `stream` (a hipStream_t; NULL for the
+ * default stream), asynchronously, with a kernel (no memset node, so it can be
+ * captured in a graph). */
+int lutgemm_workspace_init(void* d_workspace, size_t bytes, void* stream);
 
 /* Pack a BCQ matrix from the logical format into the device format.
  * Host only (CPU), deterministic: the output bytes are fully determined by
@@ -131,8 +138,9 @@ int bcq_pack_uniform(const lutgemm_shape* s, const uint8_t* codes,
  *   d_bits, d_alpha, d_offset: packed device format (d_offset only when
  *       s->has_offset, else ignored);
  *   d_x  fp16 [m][K] row-major;  d_y  fp16 [m][N] row-major, overwritten;
- *   d_workspace: at least lutgemm_workspace_size bytes (may be NULL when that
- *       size is 0); calls that overlap in time must not share a workspace.
+ *   d_workspace: at least lutgemm_workspace_size bytes, zero-filled before its
+ *       first use (may be NULL when that size is 0); calls that overlap in time
+ *       must not share a workspace.
  * Alignment (else LUTGEMM_ERR_ALIGN): d_bits, d_x and d_workspace 16 bytes,
  * d_alpha and d_offset 4 bytes, d_y 2 bytes.
  * Arithmetic: table entries, scaling and accumulation in fp32; y rounded to

@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "LutGemmError", "Shape", "lib", "abi_version", "status_string",
-    "check_shape", "packed_sizes", "workspace_size",
+    "check_shape", "packed_sizes", "workspace_size", "workspace_init",
     "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "PackedBCQ", "STATUS",
 ]
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.lutgemm_packed_sizes.argtypes = [_SHP, _SZP, _SZP, _SZP]
     L.lutgemm_workspace_size.restype = ctypes.c_int
     L.lutgemm_workspace_size.argtypes = [_SHP, ctypes.c_int32, _SZP]
+    L.lutgemm_workspace_init.restype = ctypes.c_int
+    L.lutgemm_workspace_init.argtypes = [_P, _SZ, _P]
     L.bcq_pack.restype = ctypes.c_int
     L.bcq_pack.argtypes = [_SHP, _P, _P, _P, _P, _SZ, _P, _SZ, _P, _SZ]
     L.bcq_pack_uniform.restype = ctypes.c_int
@@ -125,6 +127,11 @@ def workspace_size(N, K, q, g, has_offset, m) -> int:
     _check(lib().lutgemm_workspace_size(ctypes.byref(s), int(m), ctypes.byref(out)),
            "lutgemm_workspace_size")
     return out.value
+
+
+def workspace_init(d_workspace: int, nbytes: int, stream: Optional[int] = None):
+    """Zero-fill a device workspace on ``stream`` (required before its first use)."""
+    _check(lib().lutgemm_workspace_init(d_workspace, int(nbytes), stream), "lutgemm_workspace_init")
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -234,13 +241,16 @@ class PackedBCQ:
         return obj
 
     def workspace(self, m: int):
-        """A device workspace large enough for batch m (kept and reused)."""
+        """A zero-filled device workspace large enough for batch m (kept and reused;
+        each completed call leaves its counters zero)."""
         import torch
         need = workspace_size(self.N, self.K, self.q, self.g, self.has_offset, m)
         if need == 0:
             return None, 0
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.d_bits.device)
+            workspace_init(self._ws.data_ptr(), need,
+                           torch.cuda.current_stream(self._ws.device).cuda_stream)
         return self._ws, self._ws.numel()
 
     def __call__(self, x, out=None):

@@ -27,9 +27,12 @@
 //  * each wave keeps the loads of the next one or two input tiles in flight (a
 //    ring of register sets filled by unconditional buffer loads);
 //  * when the input dimension is split over workgroups to fill the CUs, each
-//    writes fp32 partial sums and a second kernel adds them in a fixed order:
-//    results are bitwise reproducible, and no cross-workgroup synchronisation
-//    (whose cache maintenance is costly across XCDs) is needed;
+//    writes fp32 partial sums with device-scope (write-through) stores; after
+//    its last item a workgroup waits for those stores to complete and counts
+//    its items in per-row-block arrival counters with device-scope atomics, and
+//    the last arrival of a row block adds its partials in split order (so
+//    results are bitwise reproducible). This avoids the L2-wide writeback and
+//    invalidate that release/acquire fences cost across the XCDs;
 //  * no MFMA: this is a lookup-accumulate, not a dense contraction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -47,6 +50,10 @@ namespace {
 
 constexpr int kLutWords = 256 * kChunkTile;   // one table tile: 64 KiB of fp32 entries
 constexpr int kCUs = 256;                     // MI355X compute units (dispatch heuristic)
+// Split reductions keep their arrival counters in a fixed region at the start
+// of the workspace, so any later call finds its counters zero whatever its shape.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int64_t kMaxCounters = kCounterBytes / sizeof(uint32_t);
 
 struct Params {
   const uint8_t* bits;      // packed sign bytes
@@ -55,6 +62,7 @@ struct Params {
   const uint16_t* x;        // fp16 [m][K]
   uint16_t* y;              // fp16 [m][N]
   float* partial;           // fp32 [S][m][Npad] (split reduction only)
+  uint32_t* counters;       // [n_bg][n_rb] arrivals per row block (split reduction only)
   int N, K, g, m;
   int C, KT, RT, G, S, Npad;
   int n_rb, n_bg, n_items;  // row blocks, batch groups, work items
@@ -381,7 +389,9 @@ __device__ __forceinline__ void finish_item(const Params& p, const LaneCtx& l, c
         const int row = (c.rt_first + i) * kRowTile + 4 * l.r4 + (up32 ? 2 : 0) + (up4 ? 1 : 0);
         if ((l.lane & 3) == 0) {
           if (split_mode) {
-            p.partial[((size_t)c.split * p.m + (c.r0 + r)) * p.Npad + row] = t;
+            // device-scope store: written through to where every XCD reads it
+            __hip_atomic_store(&p.partial[((size_t)c.split * p.m + (c.r0 + r)) * p.Npad + row], t,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           } else if (row < p.N) {
             p.y[(size_t)(c.r0 + r) * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)t);
           }
@@ -390,6 +400,58 @@ __device__ __forceinline__ void finish_item(const Params& p, const LaneCtx& l, c
 #pragma unroll
       for (int a = 0; a < 4; ++a) acc[r][i][a] = 0.f;
     }
+  }
+}
+
+// Split reduction, run once after a workgroup's last item (its loads have all
+// returned, so waiting costs nothing). Every wave waits until its partial-sum
+// stores are complete at device scope; then one thread per item of this
+// workgroup counts the item's arrival in its row-block counter (device-scope
+// atomics, all in flight together). An arrival that completes a row block (S
+// of them) makes this workgroup add the S partials of each of the block's rows
+// in split order, round to fp16 and store y; it also resets the counter to zero
+// for the next call. The sums of all such blocks are done in one pass.
+template <int RPW, int MC, int W>
+__device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
+  constexpr int kThreads = W * 64;
+  constexpr int kRows = W * RPW * kRowTile;   // rows per row block
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt = expcnt = lgkmcnt = 0: own stores complete
+  __syncthreads();
+  const int per = p.n_rb * p.S;
+  const int n_mine = (p.n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  for (int j0 = 0; j0 < n_mine; j0 += kThreads) {
+    const int nj = min(kThreads, n_mine - j0);
+    if ((int)threadIdx.x < nj) {
+      const int item = (int)blockIdx.x + (j0 + (int)threadIdx.x) * (int)gridDim.x;
+      const int bg = item / per;
+      const int rb = (item - bg * per) % p.n_rb;
+      uint32_t* ctr = p.counters + (size_t)bg * p.n_rb + rb;
+      const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (uint32_t)(p.S - 1);
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last[threadIdx.x] = last ? item : -1;
+    }
+    __syncthreads();
+    // every (completed block, batch row, row) of this chunk, one output per thread
+    const int per_item = MC * kRows;
+    for (int idx = threadIdx.x; idx < nj * per_item; idx += kThreads) {
+      const int j = idx / per_item;
+      const int item = s_last[j];
+      if (item < 0) continue;
+      const int rem = idx - j * per_item;
+      const int r = rem / kRows;
+      const int bg = item / per;
+      const int rb = (item - bg * per) % p.n_rb;
+      const int row = rb * kRows + (rem - r * kRows);
+      const int rr = bg * MC + r;
+      if (row >= p.N || rr >= p.m) continue;
+      float sum = 0.f;
+      for (int s = 0; s < p.S; ++s)
+        sum += __hip_atomic_load(&p.partial[((size_t)s * p.m + rr) * p.Npad + row],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p.y[(size_t)rr * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+    }
+    __syncthreads();
   }
 }
 
@@ -455,27 +517,19 @@ __global__ void __launch_bounds__(W * 64, W / 4) lutgemv_kernel(Params p) {
       }
     }
   }
-}
-
-// y[r][n] = fp16(sum over splits s = 0..S-1 of partial[s][r][n]), in that order.
-__global__ void __launch_bounds__(256) finalize_kernel(const float* __restrict__ partial,
-                                                       uint16_t* __restrict__ y, int S, int m,
-                                                       int N, int Npad) {
-  const size_t total = (size_t)m * N;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const size_t r = i / N, n = i - r * N;
-    const float* src = partial + r * Npad + n;
-    float sum = 0.f;
-    for (int s = 0; s < S; ++s) sum += src[(size_t)s * m * Npad];
-    y[i] = __builtin_bit_cast(uint16_t, (_Float16)sum);
-  }
+  if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
 }
 
 __global__ void zero_fill_kernel(uint16_t* y, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     y[i] = 0;
+}
+
+__global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -503,9 +557,19 @@ constexpr bool kInstantiated =
     (W == 16 ? (MC == 1 && GQ) : (W == 8)) &&
     kVgprEstimate<Q, RPW, MC, GQ, OFF, kRing<Q, RPW, MC, GQ, OFF, W>> <= kBudget<W>;
 
+// A deeper ring with 16 waves, when it fits (kept selectable for tuning).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
+constexpr bool kDeep16 =
+    W == 16 && MC == 1 && GQ && kVgprEstimate<Q, RPW, MC, GQ, OFF, 3> <= kBudget<W>;
+
+int g_ring_override = 0;   // tuning: 3 selects the deeper ring where it exists
+
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
 KernelFn kernel_or_null() {
   if constexpr (kInstantiated<Q, RPW, MC, GQ, OFF, W>) {
+    if constexpr (kDeep16<Q, RPW, MC, GQ, OFF, W>) {
+      if (g_ring_override == 3) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3>;
+    }
     return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRing<Q, RPW, MC, GQ, OFF, W>>;
   } else {
     return nullptr;
@@ -562,17 +626,20 @@ struct Config {
   size_t ws_bytes;
 };
 
-// Optional tuning override "RPW,S[,W[,MC]]" (LUTGEMM_TILE); never needed for correctness.
+// Optional tuning override "RPW,S[,W[,MC[,ring]]]" (LUTGEMM_TILE); never
+// needed for correctness.
 bool tile_override(int* rpw, int* s, int* w, int* mc) {
   const char* e = getenv("LUTGEMM_TILE");
+  g_ring_override = 0;
   if (!e || !*e) return false;
-  int a = 0, b = 0, c = 0, d = 0;
-  const int n = sscanf(e, "%d,%d,%d,%d", &a, &b, &c, &d);
+  int a = 0, b = 0, c = 0, d = 0, r = 0;
+  const int n = sscanf(e, "%d,%d,%d,%d,%d", &a, &b, &c, &d, &r);
   if (n < 2) return false;
   *rpw = a;
   *s = b;
   *w = n >= 3 ? c : 0;
   *mc = n >= 4 ? d : 0;
+  g_ring_override = n >= 5 ? r : 0;
   return true;
 }
 
@@ -629,7 +696,8 @@ Config choose_config(const Geometry& G, int64_t m) {
     if (os >= 1) c.S = (int)(os < G.KT ? os : (G.KT > 0 ? G.KT : 1));
   }
   if (c.S < 1) c.S = 1;
-  c.ws_bytes = c.S > 1 ? (size_t)c.S * (size_t)m * (size_t)G.Npad * sizeof(float) : 0;
+  if (c.n_rb * c.n_bg > kMaxCounters) c.S = 1;   // counters live in a fixed region
+  c.ws_bytes = c.S > 1 ? kCounterBytes + (size_t)c.S * (size_t)m * (size_t)G.Npad * sizeof(float) : 0;
   return c;
 }
 
@@ -669,6 +737,16 @@ int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes) {
   if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
   *bytes = c.ws_bytes;
   return LUTGEMM_OK;
+}
+
+int lutgemm_workspace_init(void* d_workspace, size_t bytes, void* stream) {
+  if (bytes == 0) return LUTGEMM_OK;
+  if (!d_workspace) return LUTGEMM_ERR_NULL;
+  const size_t want = (bytes + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)d_workspace, bytes);
+  return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
 }
 
 int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const void* d_alpha,
@@ -716,7 +794,8 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     p.offset = G.has_offset ? (const uint32_t*)d_offset : nullptr;
     p.x = (const uint16_t*)d_x;
     p.y = (uint16_t*)d_y;
-    p.partial = c.S > 1 ? (float*)d_workspace : nullptr;
+    p.counters = c.S > 1 ? (uint32_t*)d_workspace : nullptr;
+    p.partial = c.S > 1 ? (float*)((char*)d_workspace + kCounterBytes) : nullptr;
     p.N = (int)G.N;
     p.K = (int)G.K;
     p.g = (int)G.g;
@@ -740,14 +819,6 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     void* args[] = {&p};
     if (hipLaunchKernel((const void*)fn, grid, dim3(64 * c.W), args, 0, strm) != hipSuccess)
       return LUTGEMM_ERR_HIP;
-    if (c.S > 1) {
-      const size_t n = (size_t)m * G.N;
-      const size_t want = (n + 255) / 256;
-      const unsigned blocks = (unsigned)(want < 2048 ? want : 2048);
-      hipLaunchKernelGGL(finalize_kernel, dim3(blocks), dim3(256), 0, strm,
-                         (const float*)d_workspace, (uint16_t*)d_y, c.S, (int)m, (int)G.N,
-                         (int)G.Npad);
-    }
     return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
   } catch (...) {
     return LUTGEMM_ERR_INTERNAL;
