@@ -35,8 +35,8 @@
  * - Packed (device) format, produced by bcq_pack / bcq_pack_uniform and read
  *   by lutgemm_run. Rows are padded to Npad = 16*ceil(N/16) and 8-input
  *   chunks to 64*ceil(K/512); padding bytes and scales are zero.
- *     bits   byte   [Npad/16][ceil(K/512)][q][1024]  one block per (row tile,
- *                                input tile, plane): 64 lane blocks of 16 bytes;
+ *     bits   byte   [ceil(K/512)][Npad/16][q][1024]  one block per (input
+ *                                tile, row tile, plane): 64 lane blocks of 16 bytes;
  *                                lane block 16*r4 + c4 holds rows 4*r4 + a and
  *                                chunks 4*c4 + b (a, b < 4) at byte 4*a + b
  *     alpha  fp16   [Npad/16][K/g][q][16]

@@ -35,6 +35,20 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread"]
 
 
+def _scratch_users(remarks: str):
+    """Kernels whose resource-usage remarks report scratch (register spills)."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size:
+                out.append((name, size))
+            name = None
+    return out
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -53,18 +67,28 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     incs = [f"-I{INCLUDE}", f"-I{CSRC}"]
     tmp = tempfile.mkdtemp(prefix="lutgemm_build_")
     try:
-        pack_o = os.path.join(tmp, "pack.o")
-        kern_o = os.path.join(tmp, "lutgemv.o")
+        objs = [os.path.join(tmp, "pack.o"), os.path.join(tmp, "lutgemv.o")]
         jobs = [
-            [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "pack.cpp"), "-o", pack_o],
+            [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "pack.cpp"), "-o", objs[0]],
             [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c",
-             os.path.join(CSRC, "lutgemv.hip"), "-o", kern_o],
+             os.path.join(CSRC, "lutgemv.hip"), "-o", objs[1]],
         ]
-        with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
-            for f in [ex.submit(_run, j, verbose) for j in jobs]:
-                f.result()
+        # the kernel instances of each plane count q build in their own unit
+        for q in range(1, 9):
+            o = os.path.join(tmp, f"lutgemv_q{q}.o")
+            objs.append(o)
+            jobs.append([HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, f"-DLUTGEMM_Q={q}", "-c",
+                         "-Rpass-analysis=kernel-resource-usage",
+                         os.path.join(CSRC, "lutgemv_q.hip"), "-o", o])
+        workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            outs = [f.result() for f in [ex.submit(_run, j, False) for j in jobs]]
+        # every kernel instance is meant to fit its register budget
+        spills = [u for o in outs for u in _scratch_users(o)]
+        for name, size in spills:
+            print(f"warning: {name} uses {size} bytes of scratch per lane", file=sys.stderr)
         out_tmp = LIB_PATH + ".tmp"
-        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", pack_o, kern_o,
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
               "-pthread", "-o", out_tmp], verbose)
         os.replace(out_tmp, LIB_PATH)
     finally:

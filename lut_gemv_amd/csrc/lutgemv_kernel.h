@@ -1,0 +1,623 @@
+// lutgemv_kernel.h -- the BCQ LUT-GEMV kernel for gfx950 (MI355X): y = W_hat x
+// with W_hat held as q sign planes plus group-wise fp16 scales (and an optional offset).
+//
+// The method (LUT-GEMM, Park et al.; Elamur card "LUT-GEMM -- paper by Park et
+// al. (2022)", sections "Summary" and "Interesting ideas: Lookup tables instead
+// of multiplications"): for every 8-input chunk of x, all 256 signed sums are
+// computed once into a table; each weight byte then selects its sum, which is
+// scaled by the plane's group scale and accumulated, so the weights are never
+// expanded to fp16.
+//
+// Mapping onto CDNA4 (our design, not the pages'):
+//  * one persistent workgroup per CU (8 or 16 wave64s) walks a list of work
+//    items (row block, split of the input dimension, batch group). Tables for
+//    one input tile (64 chunks = 512 inputs) take 64 KiB of LDS: entry p of
+//    chunk t at word p*64 + t. Two such tables are kept (128 KiB), so the next
+//    step's table is built while the current one is read, with one barrier per
+//    step; the build walks each lane's entries in Gray-code order (one add per
+//    entry);
+//  * for the lookups a lane owns a 4-row x 4-chunk block of sign bytes (16
+//    bytes per plane, one 128-bit buffer load; a wave reads 1 KiB contiguously)
+//    and visits its chunks in a lane-rotated order, so the 64 lanes of every
+//    lookup read 64 different tables: no LDS bank conflicts whatever the bytes;
+//  * per lookup: one v_perm_b32 forms the LDS address from the weight byte, one
+//    ds_read_b32 and one add; when the block's four chunks share a scale group
+//    (g % 32 == 0) the four entries of a row are summed and scaled once with a
+//    v_fma_mix_f32 (fp16 scale times fp32 sum into an fp32 accumulator);
+//  * each wave keeps the loads of the next one or two input tiles in flight (a
+//    ring of register sets filled by unconditional buffer loads);
+//  * when the input dimension is split over workgroups to fill the CUs, each
+//    writes fp32 partial sums with device-scope (write-through) stores; after
+//    its last item a workgroup waits for those stores to complete and counts
+//    its items in per-row-block arrival counters with device-scope atomics, and
+//    the last arrival of a row block adds its partials in split order (so
+//    results are bitwise reproducible). This avoids the L2-wide writeback and
+//    invalidate that release/acquire fences cost across the XCDs;
+//  * no MFMA: this is a lookup-accumulate, not a dense contraction.
+//
+// Device code only. Each plane count q is instantiated in its own translation
+// unit (lutgemv_q.hip compiled with -DLUTGEMM_Q=q) so that the instances build
+// in parallel; the host launcher (lutgemv.hip) reaches them through
+// kernels_of_q<q>.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace lutgemm {
+
+constexpr int kLutWords = 256 * kChunkTile;   // one table tile: 64 KiB of fp32 entries
+constexpr int kCUs = 256;                     // MI355X compute units (dispatch heuristic)
+// Split reductions keep their arrival counters in a fixed region at the start
+// of the workspace, so any later call finds its counters zero whatever its shape.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int64_t kMaxCounters = kCounterBytes / sizeof(uint32_t);
+
+struct Params {
+  const uint8_t* bits;      // packed sign bytes
+  const uint32_t* alpha;    // packed fp16 scales, two per dword
+  const uint32_t* offset;   // packed fp16 offsets, two per dword (or null)
+  const uint16_t* x;        // fp16 [m][K]
+  uint16_t* y;              // fp16 [m][N]
+  float* partial;           // fp32 [S][m][Npad] (split reduction only)
+  uint32_t* counters;       // [n_bg][n_rb] arrivals per row block (split reduction only)
+  int N, K, g, m;
+  int C, KT, RT, G, S, Npad;
+  int n_rb, n_bg, n_items;  // row blocks, batch groups, work items
+  int g_shift;              // log2(g) when g is a power of two, else -1
+  int g_span;               // most scale groups one input tile touches
+};
+
+__device__ __forceinline__ float h2f(uint32_t word, int hi) {
+  const uint16_t bitsv = hi ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+  return (float)__builtin_bit_cast(_Float16, bitsv);
+}
+
+// Raw buffer loads: an offset at or past num_records returns zero without a
+// memory access, so row tiles past the end of the matrix and prefetches past a
+// workgroup's last tile need no branches around the loads (branches there make
+// the compiler wait for every outstanding load before the table build).
+constexpr int kBufferFlags = 0x00020000;   // dword 3 of a gfx9 raw buffer descriptor
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// ------------------------------------------------------------------ work items
+// An item is (row block, split of the input tiles, batch group), row block
+// varying fastest. Its fields are uniform over the workgroup and are computed
+// once per item (the only integer divisions of the kernel).
+struct ItemCtx {
+  int item;               // item index (>= n_items: none)
+  int kt1;                // end of the item's input tiles
+  int rt_first;           // first row tile of this wave
+  int valid_rpw;          // row tiles of this wave inside the matrix
+  int r0, rows_here;      // batch rows of the item
+  int split;
+};
+
+// Position of one input tile in a workgroup's sequence of tiles.
+struct TilePos {
+  ItemCtx c;
+  int kt;
+  bool live;              // false past the workgroup's last item: loads touch no memory
+};
+
+template <int RPW, int MC, int W>
+__device__ __forceinline__ TilePos first_tile(const Params& p, int wave, int item) {
+  TilePos t;
+  t.c.item = item;
+  t.live = item < p.n_items;
+  const int per = p.n_rb * p.S;
+  const int bg = item / per;
+  const int rem = item - bg * per;
+  t.c.split = rem / p.n_rb;
+  const int rb = rem - t.c.split * p.n_rb;
+  t.kt = t.c.split * p.KT / p.S;
+  t.c.kt1 = (t.c.split + 1) * p.KT / p.S;
+  t.c.rt_first = (rb * W + wave) * RPW;
+  t.c.valid_rpw = min(RPW, p.RT - t.c.rt_first);
+  t.c.r0 = bg * MC;
+  t.c.rows_here = t.live ? min(MC, p.m - t.c.r0) : 0;
+  return t;
+}
+
+// The tile after t: the next tile of the item, or the first tile of the
+// workgroup's next item (items advance by gridDim.x).
+template <int RPW, int MC, int W>
+__device__ __forceinline__ TilePos next_tile(const Params& p, int wave, const TilePos& t) {
+  if (t.kt + 1 < t.c.kt1) {
+    TilePos n = t;
+    n.kt = t.kt + 1;
+    return n;
+  }
+  return first_tile<RPW, MC, W>(p, wave, t.c.item + (int)gridDim.x);
+}
+
+// Lane roles. For the table build and the activations, lane l owns chunk l of
+// the input tile. For the lookups, lane l owns the lane block (r4, c4) of rows
+// 4*r4 .. +3 and chunks 4*c4 .. +3 (16 sign bytes per plane), with
+// r4 = bits 3-4 of l and c4 = bits 0-2 of l plus bit 5 of l as bit 3; it visits
+// its four chunks in the order b_k = (k + r4) & 3. At each of the four lookup
+// steps the 32 lanes of each half-wave then read 32 consecutive tables, one per
+// LDS bank, whatever the bytes are.
+struct LaneCtx {
+  int lane, wave, r4, c4;
+  uint32_t block;     // byte offset of this lane's block in a 1 KiB plane block
+  uint32_t tsel[4];   // (table index 4*c4 + b_k) * 4: byte 0 of the address
+  uint32_t psel[4];   // v_perm selector taking byte b_k of a sign word into byte 1
+};
+
+__device__ __forceinline__ LaneCtx lane_ctx() {
+  LaneCtx l;
+  l.lane = threadIdx.x & 63;
+  // wave index as a scalar: buffer descriptors built from it stay in SGPRs
+  l.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  l.r4 = (l.lane >> 3) & 3;
+  l.c4 = (l.lane & 7) | ((l.lane >> 5) << 3);
+  l.block = (uint32_t)(16 * l.r4 + l.c4) * 16u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b = (uint32_t)((k + l.r4) & 3);
+    l.tsel[k] = (4u * (uint32_t)l.c4 + b) << 2;
+    // byte 0 <- S1 byte 0 (table index), byte 1 <- S0 byte b (sign byte),
+    // byte 2 <- S1 byte 2 (table buffer), byte 3 <- 0
+    l.psel[k] = 0x0C020000u | ((4u + b) << 8);
+  }
+  return l;
+}
+
+// Everything one wave needs from memory for one input tile.
+// GQ: the four chunks of a lane block share one scale group (g % 32 == 0), so
+// scales (and offsets) are held per row; otherwise per row and visited chunk.
+template <int Q, int RPW, int MC, bool GQ, bool OFF>
+struct TileRegs {
+  static constexpr int AW = GQ ? 2 * Q : 8 * Q;   // scale dwords (fp16 pairs) per row tile
+  static constexpr int OW = OFF ? (GQ ? 2 : 8) : 0;
+  TilePos pos;
+  uint4 xv[MC];              // activations of chunk `lane`, per batch row
+  uint4 bw[RPW][Q];          // lane block per plane: word a = row 4*r4+a, byte b = chunk 4*c4+b
+  uint32_t aw[RPW][AW];      // GQ: [plane][row pair]; else [visit k][plane][row pair]
+  uint32_t ow[RPW][OW > 0 ? OW : 1];
+};
+
+__device__ __forceinline__ int group_of(const Params& p, int k) {
+  return p.g_shift >= 0 ? (k >> p.g_shift) : (k / p.g);
+}
+
+// Issue the loads of the tile at T.pos (all of them unconditional; activations
+// first, so the table build waits only for those). A dead position gives
+// zero-length ranges: the instructions issue but touch no memory.
+template <int Q, int RPW, int MC, bool GQ, bool OFF>
+__device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
+                                          TileRegs<Q, RPW, MC, GQ, OFF>& T) {
+  constexpr uint32_t kTileBytes = Q * kChunkTile * kRowTile;
+  const TilePos& t = T.pos;
+  const int k0 = t.kt * kChunkTile * 8;
+  const uint32_t kin = t.live ? (uint32_t)min(kChunkTile * 8, p.K - k0) : 0u;
+#pragma unroll
+  for (int r = 0; r < MC; ++r) {
+    const uint32_t nb = (r < t.c.rows_here) ? kin * 2u : 0u;
+    const auto xr = make_rsrc(p.x + (size_t)(t.c.r0 + r) * p.K + k0, nb);
+    T.xv[r] = load16(xr, (uint32_t)l.lane * 16u);
+  }
+  const int g_first = group_of(p, k0);
+  const uint32_t g_span = (uint32_t)min(p.G - g_first, p.g_span);
+  // group (relative to g_first) of each chunk this lane visits
+  uint32_t g_rel[GQ ? 1 : 4];
+#pragma unroll
+  for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+    const int chunk = 4 * l.c4 + (GQ ? 0 : ((k + l.r4) & 3));
+    int grp = group_of(p, k0 + 8 * chunk);
+    grp = grp < p.G - 1 ? grp : p.G - 1;
+    g_rel[k] = (uint32_t)(grp - g_first);
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const bool on = t.live && i < t.c.valid_rpw;
+    const size_t rt = (size_t)(t.c.rt_first + i);
+    const auto br = make_rsrc(p.bits + ((size_t)t.kt * p.RT + rt) * kTileBytes, on ? kTileBytes : 0u);
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      T.bw[i][q] = load16(br, (uint32_t)(q * kChunkTile * kRowTile) + l.block);
+    // scale block of (row tile, group): [plane][16 rows] fp16; this lane's four
+    // rows of plane q are 8 bytes at q*32 + 8*r4
+    const auto ar = make_rsrc(p.alpha + (rt * p.G + g_first) * (8 * Q), on ? g_span * 32u * Q : 0u);
+#pragma unroll
+    for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint2 v = load8(ar, g_rel[k] * 32u * Q + (uint32_t)(q * 32 + 8 * l.r4));
+        T.aw[i][(k * Q + q) * 2] = v.x;
+        T.aw[i][(k * Q + q) * 2 + 1] = v.y;
+      }
+    }
+    if constexpr (OFF) {
+      const auto orr = make_rsrc(p.offset + (rt * p.G + g_first) * 8, on ? g_span * 32u : 0u);
+#pragma unroll
+      for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+        const uint2 v = load8(orr, g_rel[k] * 32u + (uint32_t)(8 * l.r4));
+        T.ow[i][2 * k] = v.x;
+        T.ow[i][2 * k + 1] = v.y;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint4 xr, float (&x)[8]) {
+  x[0] = h2f(xr.x, 0); x[1] = h2f(xr.x, 1); x[2] = h2f(xr.y, 0); x[3] = h2f(xr.y, 1);
+  x[4] = h2f(xr.z, 0); x[5] = h2f(xr.z, 1); x[6] = h2f(xr.w, 0); x[7] = h2f(xr.w, 1);
+}
+
+// Table of lane l's chunk into buffer `buf`: the entries whose high nibble
+// belongs to this wave (16/W high nibbles with 16 waves, two with 8 or 12; with
+// 12 waves only the first 8 build). Entry p = sum_t (bit t of p ? +x_t : -x_t).
+// The entries are visited in Gray-code order of their varying bits, so each is
+// the previous one plus or minus 2 x_t (one add, sign known at compile time);
+// the first is summed directly.
+template <int W>
+__device__ __forceinline__ void build_table(float* lut, int buf, const LaneCtx& l, const uint4 xr) {
+  constexpr int HPW = W == 16 ? 1 : 2;        // high nibbles per building wave
+  constexpr int NB = HPW == 2 ? 5 : 4;        // pattern bits that vary within the wave
+  static_assert(W == 8 || W == 12 || W == 16, "8, 12 or 16 waves per workgroup");
+  if (W == 12 && l.wave >= 8) return;         // uniform over the wave
+  float x[8];
+  unpack8(xr, x);
+  const int h0 = l.wave * HPW;                // first high nibble (even when HPW == 2)
+  const float c = ((h0 & 1) ? x[4] : -x[4]) + ((h0 & 2) ? x[5] : -x[5]);
+  const float d = ((h0 & 4) ? x[6] : -x[6]) + ((h0 & 8) ? x[7] : -x[7]);
+  float T = (-(x[0] + x[1]) - (x[2] + x[3])) + (c + d);   // pattern h0*16: low bits clear
+  float two[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) two[t] = x[t] + x[t];       // bit 4 of the local pattern is x4
+  float* base = lut + buf * kLutWords + (h0 * 16) * kChunkTile + l.lane;
+  base[0] = T;
+#pragma unroll
+  for (int n = 1; n < (1 << NB); ++n) {
+    const int t = __builtin_ctz(n);           // the bit that flips from gray(n-1) to gray(n)
+    const int pat = n ^ (n >> 1);
+    T += ((pat >> t) & 1) ? two[t] : -two[t];
+    base[pat * kChunkTile] = T;
+  }
+}
+
+__device__ __forceinline__ float lut_at(const float* lut, uint32_t byte_addr) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + byte_addr);
+}
+
+// Look up every row tile of batch row r in table buffer `buf`. Per plane and
+// row, a lane reads the entries its four sign bytes select; with GQ they are
+// summed and scaled once, else each is scaled by its chunk's group scale.
+template <int Q, int RPW, int MC, bool GQ, bool OFF>
+__device__ __forceinline__ void lookups(const LaneCtx& l, int r, int buf, const float* lut,
+                                        const TileRegs<Q, RPW, MC, GQ, OFF>& T,
+                                        float (&acc)[MC][RPW][4]) {
+  const uint32_t bufbits = (uint32_t)buf << 16;
+  uint32_t tsel[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tsel[k] = l.tsel[k] | bufbits;
+  // offset term: entry 0xFF of a chunk's table is the sum of its 8 inputs
+  float csum[GQ ? 1 : 4];
+  if constexpr (OFF) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float e = lut_at(lut, (0xFFu << 8) | tsel[k]);
+      if constexpr (GQ) {
+        csum[0] = k == 0 ? e : csum[0] + e;
+      } else {
+        csum[k] = e;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    if (i < T.pos.c.valid_rpw) {  // uniform over the wave
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint32_t words[4] = {T.bw[i][q].x, T.bw[i][q].y, T.bw[i][q].z, T.bw[i][q].w};
+        if constexpr (GQ) {
+          // All 16 reads of the plane are issued before any is used, so that
+          // they are in flight together whatever order the scheduler keeps.
+          float e[4][4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              e[a][k] = lut_at(lut, __builtin_amdgcn_perm(words[a], tsel[k], l.psel[k]));
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const float s = (e[a][0] + e[a][1]) + (e[a][2] + e[a][3]);
+            const uint32_t aword = T.aw[i][q * 2 + (a >> 1)];
+            acc[r][i][a] = __builtin_fmaf(h2f(aword, a & 1), s, acc[r][i][a]);
+          }
+        } else {
+          // each entry has its own scale: four reads (one row) at a time
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            float e[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              e[k] = lut_at(lut, __builtin_amdgcn_perm(words[a], tsel[k], l.psel[k]));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t aword = T.aw[i][(k * Q + q) * 2 + (a >> 1)];
+              acc[r][i][a] = __builtin_fmaf(h2f(aword, a & 1), e[k], acc[r][i][a]);
+            }
+          }
+        }
+      }
+      if constexpr (OFF) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+          for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+            const uint32_t oword = T.ow[i][2 * k + (a >> 1)];
+            acc[r][i][a] = __builtin_fmaf(h2f(oword, a & 1), csum[k], acc[r][i][a]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Reduce the accumulators of a finished item over the 16 lanes that share a
+// row quad (lanes differing in bits 0-2 and 5), store them (fp16 y, or this
+// split's fp32 partials) and clear them. Each exchange halves the rows a lane
+// keeps; a lane ends with row 4*r4 + 2*bit5 + bit2 of its lane index. The
+// summation order is fixed.
+template <int RPW, int MC>
+__device__ __forceinline__ void finish_item(const Params& p, const LaneCtx& l, const ItemCtx& c,
+                                            float (&acc)[MC][RPW][4]) {
+  const bool split_mode = p.S > 1;
+  const bool up32 = (l.lane & 32) != 0, up4 = (l.lane & 4) != 0;
+#pragma unroll
+  for (int r = 0; r < MC; ++r) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      if (r < c.rows_here && i < c.valid_rpw) {
+        float v[4] = {acc[r][i][0], acc[r][i][1], acc[r][i][2], acc[r][i][3]};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float lo = v[k], hi = v[k + 2];
+          v[k] = (up32 ? hi : lo) + __shfl_xor(up32 ? lo : hi, 32, 64);
+        }
+        const float lo = v[0], hi = v[1];
+        float t = (up4 ? hi : lo) + __shfl_xor(up4 ? lo : hi, 4, 64);
+        t += __shfl_xor(t, 2, 64);
+        t += __shfl_xor(t, 1, 64);
+        const int row = (c.rt_first + i) * kRowTile + 4 * l.r4 + (up32 ? 2 : 0) + (up4 ? 1 : 0);
+        if ((l.lane & 3) == 0) {
+          if (split_mode) {
+            // device-scope store: written through to where every XCD reads it
+            __hip_atomic_store(&p.partial[((size_t)c.split * p.m + (c.r0 + r)) * p.Npad + row], t,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else if (row < p.N) {
+            p.y[(size_t)(c.r0 + r) * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)t);
+          }
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[r][i][a] = 0.f;
+    }
+  }
+}
+
+// Split reduction, run once after a workgroup's last item (its loads have all
+// returned, so waiting costs nothing). Every wave waits until its partial-sum
+// stores are complete at device scope; then one thread per item of this
+// workgroup counts the item's arrival in its row-block counter (device-scope
+// atomics, all in flight together). An arrival that completes a row block (S
+// of them) makes this workgroup add the S partials of each of the block's rows
+// in split order, round to fp16 and store y; it also resets the counter to zero
+// for the next call. The sums of all such blocks are done in one pass.
+template <int RPW, int MC, int W>
+__device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
+  constexpr int kThreads = W * 64;
+  constexpr int kRows = W * RPW * kRowTile;   // rows per row block
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt = expcnt = lgkmcnt = 0: own stores complete
+  __syncthreads();
+  const int per = p.n_rb * p.S;
+  const int n_mine = (p.n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  for (int j0 = 0; j0 < n_mine; j0 += kThreads) {
+    const int nj = min(kThreads, n_mine - j0);
+    if ((int)threadIdx.x < nj) {
+      const int item = (int)blockIdx.x + (j0 + (int)threadIdx.x) * (int)gridDim.x;
+      const int bg = item / per;
+      const int rb = (item - bg * per) % p.n_rb;
+      uint32_t* ctr = p.counters + (size_t)bg * p.n_rb + rb;
+      const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (uint32_t)(p.S - 1);
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last[threadIdx.x] = last ? item : -1;
+    }
+    __syncthreads();
+    // every (completed block, batch row, row) of this chunk, one output per thread
+    const int per_item = MC * kRows;
+    for (int idx = threadIdx.x; idx < nj * per_item; idx += kThreads) {
+      const int j = idx / per_item;
+      const int item = s_last[j];
+      if (item < 0) continue;
+      const int rem = idx - j * per_item;
+      const int r = rem / kRows;
+      const int bg = item / per;
+      const int rb = (item - bg * per) % p.n_rb;
+      const int row = rb * kRows + (rem - r * kRows);
+      const int rr = bg * MC + r;
+      if (row >= p.N || rr >= p.m) continue;
+      float sum = 0.f;
+      for (int s = 0; s < p.S; ++s)
+        sum += __hip_atomic_load(&p.partial[((size_t)s * p.m + rr) * p.Npad + row],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p.y[(size_t)rr * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+    }
+    __syncthreads();
+  }
+}
+
+// Persistent kernel: workgroup b processes items b, b + gridDim.x, ... A ring
+// of NR register sets holds the tiles in flight: at the start of each tile the
+// loads of the tile NR-1 ahead are issued into the set the previous tile used.
+// Each step (one batch row of one tile) looks up its table, builds the next
+// step's table in the other LDS buffer, and ends at the step's one barrier.
+// Q: sign planes; RPW: row tiles per wave; MC: batch rows per item; GQ: see
+// TileRegs; OFF: offset term; W: waves per workgroup (8, 12 or 16).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR>
+// The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
+// also the most that can ever run; saying so lets the scheduler use the
+// whole register budget to keep table lookups in flight.
+__global__ void __launch_bounds__(W * 64, W / 4)
+    __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) lutgemv_kernel(Params p) {
+  __shared__ float lut[2 * kLutWords];
+  using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
+
+  const LaneCtx l = lane_ctx();
+
+  float acc[MC][RPW][4];
+#pragma unroll
+  for (int r = 0; r < MC; ++r)
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[r][i][a] = 0.f;
+
+  TR R[NR];
+  R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
+  if (!R[0].pos.live) return;
+  load_tile(p, l, R[0]);
+#pragma unroll
+  for (int s = 1; s + 1 < NR; ++s) {
+    R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
+    load_tile(p, l, R[s]);
+  }
+  int buf = 0;
+  build_table<W>(lut, 0, l, R[0].xv[0]);
+  __syncthreads();
+  bool done = false;
+  while (!done) {
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      if (!done) {
+        TR& cur = R[s];
+        TR& nxt = R[(s + 1) % NR];
+        TR& pre = R[(s + NR - 1) % NR];
+        pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
+        load_tile(p, l, pre);
+#pragma unroll
+        for (int r = 0; r < MC; ++r) {
+          if (r < cur.pos.c.rows_here) {  // uniform over the workgroup
+            lookups(l, r, buf, lut, cur, acc);
+            if (r + 1 < cur.pos.c.rows_here) {
+              build_table<W>(lut, buf ^ 1, l, cur.xv[r + 1]);
+            } else if (nxt.pos.live) {
+              build_table<W>(lut, buf ^ 1, l, nxt.xv[0]);
+            }
+            __syncthreads();
+            buf ^= 1;
+          }
+        }
+        if (cur.pos.kt + 1 == cur.pos.c.kt1) finish_item<RPW, MC>(p, l, cur.pos.c, acc);
+        done = !nxt.pos.live;
+      }
+    }
+  }
+  if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+}
+
+// ------------------------------------------------------------------ instances
+
+using KernelFn = void (*)(Params);
+
+// Register budget per wave: 256 VGPRs with 8 waves (two per SIMD), 128 with 16
+// (four per SIMD). An instance keeps a ring of NR tiles in flight, the
+// accumulators and some temporaries in that budget: three tiles when they fit,
+// else two (16 waves always use two).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int NR>
+constexpr int kVgprEstimate =
+    NR * (RPW * Q * 4 + RPW * (GQ ? 2 * Q : 8 * Q) + MC * 4 + (OFF ? RPW * (GQ ? 2 : 8) : 0)) +
+    4 * RPW * MC + (GQ ? 16 : 4) + 32;   // + the table entries of one lookup group in flight
+
+template <int W>
+constexpr int kBudget = W == 16 ? 128 : 256;
+
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
+constexpr int kRing =
+    (W == 8 && kVgprEstimate<Q, RPW, MC, GQ, OFF, 3> + 8 <= kBudget<W>) ? 3 : 2;
+
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
+constexpr bool kInstantiated =
+    (W == 16 ? (MC == 1 && GQ) : (W == 8)) &&
+    kVgprEstimate<Q, RPW, MC, GQ, OFF, kRing<Q, RPW, MC, GQ, OFF, W>> <= kBudget<W>;
+
+// A deeper ring with 16 waves, when it fits (kept selectable for tuning).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
+constexpr bool kDeep16 =
+    W == 16 && MC == 1 && GQ && kVgprEstimate<Q, RPW, MC, GQ, OFF, 3> <= kBudget<W>;
+
+// ring: 3 selects the deeper ring where an instance has one (tuning), else 0.
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
+KernelFn kernel_or_null(int ring) {
+  if constexpr (kInstantiated<Q, RPW, MC, GQ, OFF, W>) {
+    if constexpr (kDeep16<Q, RPW, MC, GQ, OFF, W>) {
+      if (ring == 3) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3>;
+    }
+    return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRing<Q, RPW, MC, GQ, OFF, W>>;
+  } else {
+    (void)ring;
+    return nullptr;
+  }
+}
+
+template <int Q, int RPW, int MC, int W>
+KernelFn pick_flags(bool gq, bool off, int ring) {
+  if (gq)
+    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring)
+               : kernel_or_null<Q, RPW, MC, true, false, W>(ring);
+  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring)
+             : kernel_or_null<Q, RPW, MC, false, false, W>(ring);
+}
+
+template <int Q, int W>
+KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring) {
+  if (mc == 1) {
+    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring);
+    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring);
+  } else if (mc == 2) {
+    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring);
+    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring);
+  } else if (mc == 4) {
+    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring);
+    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring);
+  }
+  return nullptr;
+}
+
+// The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
+// item, scale groups aligned to 32 inputs (gq), an offset term (off) and w
+// waves per workgroup, or nullptr if none is built.
+template <int Q>
+KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring) {
+  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring);
+  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring);
+  return nullptr;
+}
+
+extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int);
+
+}  // namespace lutgemm

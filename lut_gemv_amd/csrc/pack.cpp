@@ -99,13 +99,24 @@ inline int64_t in_block(int64_t r, int64_t c) {
   return ((r >> 2) * 16 + (c >> 2)) * 16 + (r & 3) * 4 + (c & 3);
 }
 
+// Byte offset of the 1024-byte block of (input tile kt, row tile rt, plane i):
+// blocks are ordered input tile first, so the blocks of all row tiles for one
+// input tile are contiguous.
+inline size_t block_offset(const Geometry& G, int64_t kt, int64_t rt, int64_t i) {
+  return (((size_t)kt * G.RT + rt) * G.q + i) * (size_t)(kChunkTile * kRowTile);
+}
+
+// Zero the blocks of row tile rt (all input tiles, all planes).
+void clear_row_tile(const Geometry& G, int64_t rt, uint8_t* out) {
+  for (int64_t kt = 0; kt < G.KT; ++kt)
+    memset(out + block_offset(G, kt, rt, 0), 0, (size_t)G.q * kChunkTile * kRowTile);
+}
+
 // Scatter logical sign bytes bits[i][j][c] into the packed order; padding stays zero.
 void pack_bits(const Geometry& G, const uint8_t* bits, uint8_t* out) {
-  const int64_t tile = (int64_t)kChunkTile * kRowTile;
   parallel_for(G.RT, [&](int64_t rt0, int64_t rt1) {
     for (int64_t rt = rt0; rt < rt1; ++rt) {
-      uint8_t* base = out + (size_t)rt * G.KT * G.q * tile;
-      memset(base, 0, (size_t)G.KT * G.q * tile);
+      clear_row_tile(G, rt, out);
       const int64_t rows = (G.N - rt * kRowTile) < kRowTile ? (G.N - rt * kRowTile) : kRowTile;
       for (int64_t r = 0; r < rows; ++r) {
         const int64_t j = rt * kRowTile + r;
@@ -113,7 +124,7 @@ void pack_bits(const Geometry& G, const uint8_t* bits, uint8_t* out) {
           const uint8_t* src = bits + ((size_t)i * G.N + j) * G.C;
           for (int64_t c = 0; c < G.C; ++c) {
             const int64_t kt = c / kChunkTile, cl = c % kChunkTile;
-            base[(kt * G.q + i) * kChunkTile * kRowTile + in_block(r, cl)] = src[c];
+            out[block_offset(G, kt, rt, i) + in_block(r, cl)] = src[c];
           }
         }
       }
@@ -246,12 +257,10 @@ int bcq_pack_uniform(const lutgemm_shape* s, const uint8_t* codes, const uint16_
     }
 
     // ---- sign planes: plane i holds bit i of each code
-    const int64_t tile = (int64_t)kChunkTile * kRowTile;
     if (G.bits_bytes) {
       parallel_for(G.RT, [&](int64_t rt0, int64_t rt1) {
         for (int64_t rt = rt0; rt < rt1; ++rt) {
-          uint8_t* base = out_bits + (size_t)rt * G.KT * G.q * tile;
-          memset(base, 0, (size_t)G.KT * G.q * tile);
+          clear_row_tile(G, rt, out_bits);
           const int64_t rows = (G.N - rt * kRowTile) < kRowTile ? (G.N - rt * kRowTile) : kRowTile;
           for (int64_t r = 0; r < rows; ++r) {
             const uint8_t* row = codes + (size_t)(rt * kRowTile + r) * G.K;
@@ -260,7 +269,7 @@ int bcq_pack_uniform(const lutgemm_shape* s, const uint8_t* codes, const uint16_
               for (int64_t i = 0; i < G.q; ++i) {
                 unsigned byte = 0;
                 for (int t = 0; t < 8; ++t) byte |= ((row[8 * c + t] >> i) & 1u) << t;
-                base[(kt * G.q + i) * kChunkTile * kRowTile + in_block(r, cl)] = (uint8_t)byte;
+                out_bits[block_offset(G, kt, rt, i) + in_block(r, cl)] = (uint8_t)byte;
               }
             }
           }

@@ -259,10 +259,10 @@ def pack(bits, alpha, offset, g: int):
 
     * rows are padded to a multiple of 16 (padding: sign bytes 0, scales 0);
       chunks (8 inputs) are padded to a multiple of 64 (padding bytes 0);
-    * bits: per (row tile rt, input tile kt, plane i) a block of 1024 bytes
-      made of 64 lane blocks of 16 bytes. Lane block L = 16*r4 + c4 covers rows
-      16 rt + 4 r4 + a and chunks 64 kt + 4 c4 + b (a, b in 0..3); its byte
-      4 a + b is ``bits[i][16 rt + 4 r4 + a][64 kt + 4 c4 + b]``;
+    * bits: per (input tile kt, row tile rt, plane i), in that order, a block
+      of 1024 bytes made of 64 lane blocks of 16 bytes. Lane block L = 16*r4 +
+      c4 covers rows 16 rt + 4 r4 + a and chunks 64 kt + 4 c4 + b (a, b in
+      0..3); its byte 4 a + b is ``bits[i][16 rt + 4 r4 + a][64 kt + 4 c4 + b]``;
     * alpha : fp16 ``[rt][grp][i][r]`` = ``alpha[i][16 rt + r][grp]``;
     * offset: fp16 ``[rt][grp][r]`` = ``offset[16 rt + r][grp]``.
 
@@ -273,7 +273,7 @@ def pack(bits, alpha, offset, g: int):
     G = alpha.shape[2]
     RT = -(-N // ROW_TILE)
     KT = -(-C // CHUNK_TILE)
-    out_b = np.zeros((RT, KT, q, 4, 16, 4, 4), np.uint8)    # [rt][kt][i][r4][c4][a][b]
+    out_b = np.zeros((KT, RT, q, 4, 16, 4, 4), np.uint8)    # [kt][rt][i][r4][c4][a][b]
     out_a = np.zeros((RT, G, q, ROW_TILE), np.uint16)
     out_o = np.zeros((RT, G, ROW_TILE), np.uint16)
     a16 = np.asarray(alpha, dtype=np.float16).view(np.uint16)
@@ -286,7 +286,7 @@ def pack(bits, alpha, offset, g: int):
                 block[:r_hi, :c_hi] = bits[i, rt * ROW_TILE:rt * ROW_TILE + r_hi,
                                            kt * CHUNK_TILE:kt * CHUNK_TILE + c_hi]
                 # row 4 r4 + a, chunk 4 c4 + b  ->  [r4][c4][a][b]
-                out_b[rt, kt, i] = block.reshape(4, 4, 16, 4).transpose(0, 2, 1, 3)
+                out_b[kt, rt, i] = block.reshape(4, 4, 16, 4).transpose(0, 2, 1, 3)
         r_hi = min(ROW_TILE, N - rt * ROW_TILE)
         rows = slice(rt * ROW_TILE, rt * ROW_TILE + r_hi)
         for grp in range(G):

@@ -292,7 +292,7 @@ def _unpack_by_loops(pb, pa, po, q, N, K, g):
     for rt in range(RT):
         for kt in range(KT):
             for i in range(q):
-                base = ((rt * KT + kt) * q + i) * 1024
+                base = ((kt * RT + rt) * q + i) * 1024
                 for lane in range(64):
                     r4, c4 = lane // 16, lane % 16
                     for a in range(4):
@@ -334,18 +334,18 @@ def test_pack_roundtrip(N, K, q, g, off):
 
 def test_pack_single_bit_positions():
     """Hand-placed bytes land where the layout definition says: block
-    ((rt*KT + kt)*q + i)*1024, lane block 16*(16*r4 + c4), byte 4*a + b for
+    ((kt*RT + rt)*q + i)*1024, lane block 16*(16*r4 + c4), byte 4*a + b for
     row 16 rt + 4 r4 + a and chunk 64 kt + 4 c4 + b."""
     q, N, K, g = 2, 20, 1024, 256
     bits = np.zeros((q, N, K // 8), np.uint8)
     cases = {
         # (plane, row, chunk): row 17 -> rt 1, r4 0, a 1; chunk 70 -> kt 1, c4 1, b 2
-        (1, 17, 70): ((1 * 2 + 1) * 2 + 1) * 1024 + 16 * (16 * 0 + 1) + 4 * 1 + 2,
+        (1, 17, 70): ((1 * 2 + 1) * 2 + 1) * 1024 + 16 * (16 * 0 + 1) + 4 * 1 + 2,   # kt 1, rt 1
         (0, 0, 0): 0,
         # row 15 -> rt 0, r4 3, a 3; chunk 63 -> kt 0, c4 15, b 3
         (0, 15, 63): 16 * (16 * 3 + 15) + 4 * 3 + 3,
         # row 3 -> r4 0, a 3; chunk 127 -> kt 1, c4 15, b 3
-        (1, 3, 127): ((0 * 2 + 1) * 2 + 1) * 1024 + 16 * 15 + 4 * 3 + 3,
+        (1, 3, 127): ((1 * 2 + 0) * 2 + 1) * 1024 + 16 * 15 + 4 * 3 + 3,    # kt 1, rt 0
         # row 6 -> r4 1, a 2; chunk 9 -> kt 0, c4 2, b 1
         (0, 6, 9): 16 * (16 * 1 + 2) + 4 * 2 + 1,
     }
