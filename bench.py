@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("µs/GEMV + achieved HBM GB/s, K=12288 N=49152 3-bit BCQ g=128, batch 1")
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "lut_gemv_amd", "csrc", "lutgemv.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "lut_gemv_amd", "csrc", f)
+               for f in ("lutgemv_kernel.h", "lutgemv_q.hip", "lutgemv.hip", "layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lutgemv_traffic.json")
 
 
@@ -44,8 +45,12 @@ def algorithmic_bytes(N, K, q, g, m, has_offset):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel and launcher sources (traffic counters go stale when they change)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic():
@@ -86,12 +91,16 @@ def load_workload(name):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed launches first (the clocks take a few hundred to settle)")
     ap.add_argument("--workload", default="opt175b_ffn_up")
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct weight copies cycled through (0: enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the timed region, copy MIB MiB device to device 5 times "
+                         "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -143,27 +152,42 @@ def main():
         lg.lutgemm_run(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(),
                        ws.data_ptr() if ws_bytes else None, ws_bytes, sh)
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 device copies of {n} bytes")
+        del src, dst
     torch.cuda.synchronize()
     log(f"{R} rotating weight copies ({R * weight_bytes / 2**30:.2f} GiB); warmup {args.warmup}")
     for k in range(args.warmup):
         launch(k)
     torch.cuda.synchronize()
 
+    # timed region: K back-to-back products, wall clock between two synchronizations
     K_steps = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
     torch.cuda.synchronize()
     t_begin = time.perf_counter()
+    for k in range(K_steps):
+        launch(k)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_begin
+    # kernel durations: the same K launches again, each between two HIP events
+    # recorded on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
     for k in range(K_steps):
         starts[k].record(stream)
         launch(k)
         ends[k].record(stream)
     torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_begin
     durs_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    log(f"timed {K_steps} steps in {t_total * 1e3:.2f} ms; per-launch event median "
-        f"{np.median(durs_ms) * 1e3:.2f} us, p10 {np.percentile(durs_ms, 10) * 1e3:.2f}, "
-        f"p90 {np.percentile(durs_ms, 90) * 1e3:.2f}")
+    log(f"timed {K_steps} steps in {t_total * 1e3:.2f} ms; per-launch event mean "
+        f"{durs_ms.mean() * 1e3:.2f} us, median {np.median(durs_ms) * 1e3:.2f}, "
+        f"p10 {np.percentile(durs_ms, 10) * 1e3:.2f}, p90 {np.percentile(durs_ms, 90) * 1e3:.2f}")
 
     ms_per_step = t_total * 1e3 / K_steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -190,6 +214,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_gemv": round(ms_per_step * 1e3, 2),
+        "us_per_gemv_kernel_mean": round(float(durs_ms.mean()) * 1e3, 2),
         "us_per_gemv_kernel_median": round(float(np.median(durs_ms)) * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",

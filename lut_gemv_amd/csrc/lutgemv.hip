@@ -49,25 +49,27 @@ KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w) {
 
 struct Config {
   int RPW, MC, S, W;
+  int RI;                // row tiles per row block (<= W * RPW)
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
 };
 
-// Optional tuning override "RPW,S[,W[,MC[,ring]]]" (LUTGEMM_TILE); never
+// Optional tuning override "RPW,S[,W[,MC[,ring[,RI]]]]" (LUTGEMM_TILE); never
 // needed for correctness.
-bool tile_override(int* rpw, int* s, int* w, int* mc) {
+bool tile_override(int* rpw, int* s, int* w, int* mc, int* ri) {
   const char* e = getenv("LUTGEMM_TILE");
   g_ring_override = 0;
   if (!e || !*e) return false;
-  int a = 0, b = 0, c = 0, d = 0, r = 0;
-  const int n = sscanf(e, "%d,%d,%d,%d,%d", &a, &b, &c, &d, &r);
+  int a = 0, b = 0, c = 0, d = 0, r = 0, t = 0;
+  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d", &a, &b, &c, &d, &r, &t);
   if (n < 2) return false;
   *rpw = a;
   *s = b;
   *w = n >= 3 ? c : 0;
   *mc = n >= 4 ? d : 0;
   g_ring_override = n >= 5 ? r : 0;
+  *ri = n >= 6 ? t : 0;
   return true;
 }
 
@@ -104,21 +106,23 @@ Config choose_config(const Geometry& G, int64_t m) {
         c.W = v.w;
         c.RPW = v.rpw;
         c.MC = v.mc;
+        c.RI = (int)rows;
         c.n_rb = n_rb;
         c.n_bg = n_bg;
         c.S = (int)s;
       }
     }
   }
-  int orpw = 0, os = 0, ow = 0, omc = 0;
-  if (tile_override(&orpw, &os, &ow, &omc)) {
+  int orpw = 0, os = 0, ow = 0, omc = 0, ori = 0;
+  if (tile_override(&orpw, &os, &ow, &omc, &ori)) {
     const int w = ow ? ow : c.W;
     const int mc = omc ? omc : c.MC;
     if (pick_kernel((int)G.q, orpw, mc, c.gq, G.has_offset, w)) {
       c.W = w;
       c.RPW = orpw;
       c.MC = mc;
-      c.n_rb = (G.RT + (int64_t)c.W * c.RPW - 1) / ((int64_t)c.W * c.RPW);
+      c.RI = (ori >= 1 && ori <= c.W * c.RPW) ? ori : c.W * c.RPW;
+      c.n_rb = (G.RT + c.RI - 1) / c.RI;
       c.n_bg = (m + c.MC - 1) / c.MC;
     }
     if (os >= 1) c.S = (int)(os < G.KT ? os : (G.KT > 0 ? G.KT : 1));
@@ -235,6 +239,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     p.S = c.S;
     p.Npad = (int)G.Npad;
     p.n_rb = (int)c.n_rb;
+    p.ri = c.RI;
     p.g_shift = -1;
     for (int b = 3; b < 31; ++b)
       if (((int64_t)1 << b) == G.g) p.g_shift = b;

@@ -65,6 +65,7 @@ struct Params {
   int N, K, g, m;
   int C, KT, RT, G, S, Npad;
   int n_rb, n_bg, n_items;  // row blocks, batch groups, work items
+  int ri;                   // row tiles per row block (at most waves * RPW)
   int g_shift;              // log2(g) when g is a power of two, else -1
   int g_span;               // most scale groups one input tile touches
 };
@@ -125,8 +126,8 @@ __device__ __forceinline__ TilePos first_tile(const Params& p, int wave, int ite
   const int rb = rem - t.c.split * p.n_rb;
   t.kt = t.c.split * p.KT / p.S;
   t.c.kt1 = (t.c.split + 1) * p.KT / p.S;
-  t.c.rt_first = (rb * W + wave) * RPW;
-  t.c.valid_rpw = min(RPW, p.RT - t.c.rt_first);
+  t.c.rt_first = rb * p.ri + wave * RPW;
+  t.c.valid_rpw = min(min(RPW, p.ri - wave * RPW), p.RT - t.c.rt_first);
   t.c.r0 = bg * MC;
   t.c.rows_here = t.live ? min(MC, p.m - t.c.r0) : 0;
   return t;
@@ -423,7 +424,7 @@ __device__ __forceinline__ void finish_item(const Params& p, const LaneCtx& l, c
 template <int RPW, int MC, int W>
 __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
   constexpr int kThreads = W * 64;
-  constexpr int kRows = W * RPW * kRowTile;   // rows per row block
+  const int kRows = p.ri * kRowTile;   // rows per row block
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt = expcnt = lgkmcnt = 0: own stores complete
   __syncthreads();
   const int per = p.n_rb * p.S;
