@@ -43,7 +43,9 @@
  *     offset fp16   [Npad/16][K/g][16]
  * - Shape rules (else LUTGEMM_ERR_SHAPE): N >= 0, K >= 0, K % 8 == 0,
  *   1 <= q <= 8, g >= 8, g % 8 == 0, K % g == 0 (when K > 0),
- *   has_offset in {0, 1}, N and K below 2^30, 0 <= m <= 65535.
+ *   has_offset in {0, 1}, N and K below 2^30, 0 <= m <= 65535. For
+ *   lutgemm_run and lutgemm_workspace_size, each of the packed bits, packed
+ *   alpha, packed offset and x (m*K fp16) must also be smaller than 4 GiB.
  */
 #ifndef LUTGEMM_H
 #define LUTGEMM_H

@@ -30,10 +30,8 @@ __global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
 
 // ------------------------------------------------------------------ dispatch
 
-int g_ring_override = 0;   // tuning: 3 selects the deeper ring where it exists
-
-KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w) {
-  const int ring = g_ring_override;
+// ring: 3 asks for the 3-deep ring where an instance has one, 0 for the default.
+KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring) {
   switch (q) {
     case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring);
     case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring);
@@ -50,82 +48,103 @@ KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w) {
 struct Config {
   int RPW, MC, S, W;
   int RI;                // row tiles per row block (<= W * RPW)
+  int ring;              // 3: the 3-deep ring; 0: the instance's default
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
 };
 
+struct TileOverride {
+  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0;
+};
+
 // Optional tuning override "RPW,S[,W[,MC[,ring[,RI]]]]" (LUTGEMM_TILE); never
 // needed for correctness.
-bool tile_override(int* rpw, int* s, int* w, int* mc, int* ri) {
+bool tile_override(TileOverride* o) {
   const char* e = getenv("LUTGEMM_TILE");
-  g_ring_override = 0;
   if (!e || !*e) return false;
-  int a = 0, b = 0, c = 0, d = 0, r = 0, t = 0;
-  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d", &a, &b, &c, &d, &r, &t);
-  if (n < 2) return false;
-  *rpw = a;
-  *s = b;
-  *w = n >= 3 ? c : 0;
-  *mc = n >= 4 ? d : 0;
-  g_ring_override = n >= 5 ? r : 0;
-  *ri = n >= 6 ? t : 0;
-  return true;
+  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring, &o->ri);
+  return n >= 2;
 }
 
-// Pick waves, rows per wave, batch rows per item and the split of the input
-// tiles. The kernel is persistent (one workgroup per CU, LDS-bound), so each
-// CU works through ceil(items / kCUs) items. The estimate charges each item
-// its tiles, weighted by the row tiles it covers and its batch rows (a tile
-// step of 16 row tiles is one unit; 8-wave instances pay for their lower
-// latency hiding), plus a small cost per item and one for the extra
-// reduction kernel a split needs.
+// Pick waves, rows per wave, batch rows per item, row tiles per item, the
+// split of the input tiles and the ring depth. The kernel is persistent (one
+// workgroup per CU, LDS-bound), so each CU works through ceil(items / kCUs)
+// items.
+//
+// Batch 1 with grouped scales (the HBM-bound case): when the matrix has
+// between 8 and 16 row tiles per CU, each CU takes one row block of
+// ceil(row tiles / CUs) row tiles over the whole input dimension, with 16
+// waves and a 3-deep ring. All CUs then stream the same input tile window in
+// step (the best access pattern measured), with no split reduction.
+//
+// Otherwise a cost estimate charges each item its tiles, weighted by the row
+// tiles it covers and its batch rows (a tile step of 16 row tiles is one unit;
+// 8-wave instances pay for their lower latency hiding), plus a small cost per
+// item and one for the split reduction.
 Config choose_config(const Geometry& G, int64_t m) {
   Config c{};
   c.gq = (G.g % 32) == 0;
   c.W = 0;   // stays 0 if no instance fits (reported as an internal error)
-  double best = 1e300;
-  struct Cand { int w, rpw, mc; double eff; };
-  const Cand cands[] = {{16, 2, 1, 1.0}, {16, 1, 1, 1.0}, {8, 2, 4, 1.3}, {8, 1, 4, 1.3},
-                        {8, 2, 2, 1.3}, {8, 1, 2, 1.3}, {8, 2, 1, 1.3}, {8, 1, 1, 1.3}};
-  for (const Cand& v : cands) {
-    if (v.mc > 1 && m < v.mc) continue;
-    if (!pick_kernel((int)G.q, v.rpw, v.mc, c.gq, G.has_offset, v.w)) continue;
-    const int64_t rows = (int64_t)v.w * v.rpw;            // row tiles per item
-    const int64_t n_rb = (G.RT + rows - 1) / rows;
-    const int64_t n_bg = (m + v.mc - 1) / v.mc;
-    const int64_t smax = G.KT < 64 ? G.KT : 64;
-    for (int64_t s = 1; s <= smax; ++s) {
-      const int64_t items = n_rb * n_bg * s;
-      const int64_t per_cu = (items + kCUs - 1) / kCUs;
-      const int64_t tiles = (G.KT + s - 1) / s;
-      const double unit = v.eff * (double)rows * v.mc / 16.0;
-      const double cost = (double)per_cu * (tiles * unit + 0.3 * unit) + (s > 1 ? 2.0 : 0.0);
-      if (cost < best - 1e-9) {
-        best = cost;
-        c.W = v.w;
-        c.RPW = v.rpw;
-        c.MC = v.mc;
-        c.RI = (int)rows;
-        c.n_rb = n_rb;
-        c.n_bg = n_bg;
-        c.S = (int)s;
+  c.ring = 0;
+  const int q = (int)G.q;
+  const bool off = G.has_offset;
+  const int64_t ri1 = (G.RT + kCUs - 1) / kCUs;
+  if (m == 1 && c.gq && ri1 >= 8 && ri1 <= 16 && pick_kernel(q, 1, 1, true, off, 16, 3) &&
+      pick_kernel(q, 1, 1, true, off, 16, 3) != pick_kernel(q, 1, 1, true, off, 16, 0)) {
+    c.W = 16;
+    c.RPW = 1;
+    c.MC = 1;
+    c.RI = (int)ri1;
+    c.ring = 3;
+    c.n_rb = (G.RT + ri1 - 1) / ri1;
+    c.n_bg = 1;
+    c.S = 1;
+  } else {
+    double best = 1e300;
+    struct Cand { int w, rpw, mc; double eff; };
+    const Cand cands[] = {{16, 2, 1, 1.0}, {16, 1, 1, 1.0}, {8, 2, 4, 1.3}, {8, 1, 4, 1.3},
+                          {8, 2, 2, 1.3}, {8, 1, 2, 1.3}, {8, 2, 1, 1.3}, {8, 1, 1, 1.3}};
+    for (const Cand& v : cands) {
+      if (v.mc > 1 && m < v.mc) continue;
+      if (!pick_kernel(q, v.rpw, v.mc, c.gq, off, v.w, 0)) continue;
+      const int64_t rows = (int64_t)v.w * v.rpw;            // row tiles per item
+      const int64_t n_rb = (G.RT + rows - 1) / rows;
+      const int64_t n_bg = (m + v.mc - 1) / v.mc;
+      const int64_t smax = G.KT < 64 ? G.KT : 64;
+      for (int64_t s = 1; s <= smax; ++s) {
+        const int64_t items = n_rb * n_bg * s;
+        const int64_t per_cu = (items + kCUs - 1) / kCUs;
+        const int64_t tiles = (G.KT + s - 1) / s;
+        const double unit = v.eff * (double)rows * v.mc / 16.0;
+        const double cost = (double)per_cu * (tiles * unit + 0.3 * unit) + (s > 1 ? 2.0 : 0.0);
+        if (cost < best - 1e-9) {
+          best = cost;
+          c.W = v.w;
+          c.RPW = v.rpw;
+          c.MC = v.mc;
+          c.RI = (int)rows;
+          c.n_rb = n_rb;
+          c.n_bg = n_bg;
+          c.S = (int)s;
+        }
       }
     }
   }
-  int orpw = 0, os = 0, ow = 0, omc = 0, ori = 0;
-  if (tile_override(&orpw, &os, &ow, &omc, &ori)) {
-    const int w = ow ? ow : c.W;
-    const int mc = omc ? omc : c.MC;
-    if (pick_kernel((int)G.q, orpw, mc, c.gq, G.has_offset, w)) {
+  TileOverride o;
+  if (tile_override(&o)) {
+    const int w = o.w ? o.w : c.W;
+    const int mc = o.mc ? o.mc : c.MC;
+    if (pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring)) {
       c.W = w;
-      c.RPW = orpw;
+      c.RPW = o.rpw;
       c.MC = mc;
-      c.RI = (ori >= 1 && ori <= c.W * c.RPW) ? ori : c.W * c.RPW;
+      c.ring = o.ring;
+      c.RI = (o.ri >= 1 && o.ri <= c.W * c.RPW) ? o.ri : c.W * c.RPW;
       c.n_rb = (G.RT + c.RI - 1) / c.RI;
       c.n_bg = (m + c.MC - 1) / c.MC;
     }
-    if (os >= 1) c.S = (int)(os < G.KT ? os : (G.KT > 0 ? G.KT : 1));
+    if (o.s >= 1) c.S = (int)(o.s < G.KT ? o.s : (G.KT > 0 ? G.KT : 1));
   }
   if (c.S < 1) c.S = 1;
   if (c.n_rb * c.n_bg > kMaxCounters) c.S = 1;   // counters live in a fixed region
@@ -150,6 +169,14 @@ int check_device() {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// The kernel addresses each input buffer with 32-bit offsets from its base
+// (descriptor sizes are offset + extent, so the buffers stay below 4 GiB).
+bool buffers_fit(const Geometry& G, int64_t m) {
+  const uint64_t lim = 0xFFFFFFFFull;
+  return G.bits_bytes <= lim && G.alpha_count * 2 <= lim && G.offset_count * 2 <= lim &&
+         (uint64_t)m * (uint64_t)G.K * 2 <= lim;
+}
+
 }  // namespace
 }  // namespace lutgemm
 
@@ -164,6 +191,7 @@ int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes) {
   if (m < 0 || m > kMaxBatch) return LUTGEMM_ERR_SHAPE;
   Geometry G = geometry(s);
   *bytes = 0;
+  if (!buffers_fit(G, m)) return LUTGEMM_ERR_SHAPE;
   if (m == 0 || G.N == 0 || G.K == 0) return LUTGEMM_OK;
   const Config c = choose_config(G, m);
   if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
@@ -189,6 +217,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     if (st) return st;
     if (m < 0 || m > kMaxBatch) return LUTGEMM_ERR_SHAPE;
     Geometry G = geometry(s);
+    if (!buffers_fit(G, m)) return LUTGEMM_ERR_SHAPE;
     if (m == 0 || G.N == 0) return LUTGEMM_OK;
     if (!d_y) return LUTGEMM_ERR_NULL;
     if (!aligned(d_y, 2)) return LUTGEMM_ERR_ALIGN;
@@ -218,7 +247,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
       return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
     }
 
-    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W);
+    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring);
     if (!fn) return LUTGEMM_ERR_INTERNAL;
     Params p{};
     p.bits = (const uint8_t*)d_bits;
@@ -244,6 +273,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     for (int b = 3; b < 31; ++b)
       if (((int64_t)1 << b) == G.g) p.g_shift = b;
     p.g_span = (int)((kChunkTile * 8 + G.g - 1) / G.g + 1);
+    p.g_tile = (kChunkTile * 8) % G.g == 0 ? 1 : 0;
     p.n_bg = (int)c.n_bg;
     const int64_t items = c.n_rb * c.n_bg * c.S;
     if (items > 0x7FFFFFFF - kCUs) return LUTGEMM_ERR_SHAPE;

@@ -68,6 +68,7 @@ struct Params {
   int ri;                   // row tiles per row block (at most waves * RPW)
   int g_shift;              // log2(g) when g is a power of two, else -1
   int g_span;               // most scale groups one input tile touches
+  int g_tile;               // 1 if g divides 512: every input tile starts a group
 };
 
 __device__ __forceinline__ float h2f(uint32_t word, int hi) {
@@ -81,17 +82,27 @@ __device__ __forceinline__ float h2f(uint32_t word, int hi) {
 // the compiler wait for every outstanding load before the table build).
 constexpr int kBufferFlags = 0x00020000;   // dword 3 of a gfx9 raw buffer descriptor
 
+// Buffer descriptors and scalar offsets must live in scalar registers; the
+// values put there are uniform over the wave, and readfirstlane says so (it
+// is free for a value already in a scalar register, and otherwise replaces a
+// loop over distinct lane values by one instruction).
+__device__ __forceinline__ uint32_t uni(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)uni(nbytes),
                                            kBufferFlags);
 }
 
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+// The range check covers voff (per lane) plus soff (scalar): a descriptor
+// whose num_records is soff + n admits exactly voff < n.
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, uni(soff), 0));
 }
 
-__device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+__device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, uni(soff), 0));
 }
 
 // ------------------------------------------------------------------ work items
@@ -102,7 +113,8 @@ struct ItemCtx {
   int item;               // item index (>= n_items: none)
   int kt1;                // end of the item's input tiles
   int rt_first;           // first row tile of this wave
-  int valid_rpw;          // row tiles of this wave inside the matrix
+  int valid_rpw;          // row tiles of this wave inside the matrix (may be <= 0)
+  int nrt;                // row tiles this wave reads: 0 .. RPW, 0 when there is no item
   int r0, rows_here;      // batch rows of the item
   int split;
 };
@@ -128,6 +140,8 @@ __device__ __forceinline__ TilePos first_tile(const Params& p, int wave, int ite
   t.c.kt1 = (t.c.split + 1) * p.KT / p.S;
   t.c.rt_first = rb * p.ri + wave * RPW;
   t.c.valid_rpw = min(min(RPW, p.ri - wave * RPW), p.RT - t.c.rt_first);
+  // uniform over the wave: keep it (and the descriptors sized by it) scalar
+  t.c.nrt = __builtin_amdgcn_readfirstlane(t.live ? max(t.c.valid_rpw, 0) : 0);
   t.c.r0 = bg * MC;
   t.c.rows_here = t.live ? min(MC, p.m - t.c.r0) : 0;
   return t;
@@ -157,6 +171,8 @@ struct LaneCtx {
   uint32_t block;     // byte offset of this lane's block in a 1 KiB plane block
   uint32_t tsel[4];   // (table index 4*c4 + b_k) * 4: byte 0 of the address
   uint32_t psel[4];   // v_perm selector taking byte b_k of a sign word into byte 1
+  uint32_t aoff, ooff;  // g % 32 == 0 and g divides 512: byte offset of this lane's
+                        // scales (and offsets) in a tile's scale block
 };
 
 __device__ __forceinline__ LaneCtx lane_ctx() {
@@ -196,6 +212,16 @@ __device__ __forceinline__ int group_of(const Params& p, int k) {
   return p.g_shift >= 0 ? (k >> p.g_shift) : (k / p.g);
 }
 
+// When g divides 512 every input tile starts a group, so the group of a lane's
+// chunks (one group when g % 32 == 0), relative to the tile's first group, is
+// the same for every tile: the lane's scale offsets are computed once.
+template <int Q>
+__device__ __forceinline__ void tile_group_offsets(const Params& p, LaneCtx& l) {
+  const uint32_t g_rel = p.g_tile ? (uint32_t)((32 * l.c4) >> p.g_shift) : 0u;
+  l.aoff = g_rel * 32u * Q + 8u * (uint32_t)l.r4;
+  l.ooff = g_rel * 32u + 8u * (uint32_t)l.r4;
+}
+
 // Issue the loads of the tile at T.pos (all of them unconditional; activations
 // first, so the table build waits only for those). A dead position gives
 // zero-length ranges: the instructions issue but touch no memory.
@@ -203,51 +229,67 @@ template <int Q, int RPW, int MC, bool GQ, bool OFF>
 __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
                                           TileRegs<Q, RPW, MC, GQ, OFF>& T) {
   constexpr uint32_t kTileBytes = Q * kChunkTile * kRowTile;
+  constexpr int NV = GQ ? 1 : 4;
   const TilePos& t = T.pos;
   const int k0 = t.kt * kChunkTile * 8;
+  // Every descriptor starts at its buffer's base and ends after this tile's
+  // bytes for this wave; the tile's position goes in the scalar offset (each
+  // buffer is under 4 GiB). A dead position is an empty range.
   const uint32_t kin = t.live ? (uint32_t)min(kChunkTile * 8, p.K - k0) : 0u;
 #pragma unroll
   for (int r = 0; r < MC; ++r) {
     const uint32_t nb = (r < t.c.rows_here) ? kin * 2u : 0u;
-    const auto xr = make_rsrc(p.x + (size_t)(t.c.r0 + r) * p.K + k0, nb);
-    T.xv[r] = load16(xr, (uint32_t)l.lane * 16u);
+    const uint32_t xs = ((uint32_t)(t.c.r0 + r) * (uint32_t)p.K + (uint32_t)k0) * 2u;
+    T.xv[r] = load16(make_rsrc(p.x, nb ? xs + nb : 0u), (uint32_t)l.lane * 16u, xs);
   }
+  // sign blocks of this wave's row tiles (adjacent in the input-tile-first order)
+  const int nrt = t.live ? t.c.nrt : 0;
+  const uint32_t bs = ((uint32_t)t.kt * (uint32_t)p.RT + (uint32_t)t.c.rt_first) * kTileBytes;
+  const auto br = make_rsrc(p.bits, nrt ? bs + (uint32_t)nrt * kTileBytes : 0u);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      T.bw[i][q] = load16(br, (uint32_t)(i * kTileBytes + q * kChunkTile * kRowTile) + l.block, bs);
   const int g_first = group_of(p, k0);
   const uint32_t g_span = (uint32_t)min(p.G - g_first, p.g_span);
-  // group (relative to g_first) of each chunk this lane visits
-  uint32_t g_rel[GQ ? 1 : 4];
+  // byte offset of the scales (offsets) of each chunk this lane visits
+  uint32_t aoff[NV], ooff[NV];
 #pragma unroll
-  for (int k = 0; k < (GQ ? 1 : 4); ++k) {
-    const int chunk = 4 * l.c4 + (GQ ? 0 : ((k + l.r4) & 3));
-    int grp = group_of(p, k0 + 8 * chunk);
-    grp = grp < p.G - 1 ? grp : p.G - 1;
-    g_rel[k] = (uint32_t)(grp - g_first);
+  for (int k = 0; k < NV; ++k) {
+    if (GQ && p.g_tile) {
+      aoff[k] = l.aoff;
+      ooff[k] = l.ooff;
+    } else {
+      const int chunk = 4 * l.c4 + (GQ ? 0 : ((k + l.r4) & 3));
+      int grp = group_of(p, k0 + 8 * chunk);
+      grp = grp < p.G - 1 ? grp : p.G - 1;
+      const uint32_t g_rel = (uint32_t)(grp - g_first);
+      aoff[k] = g_rel * 32u * Q + 8u * (uint32_t)l.r4;
+      ooff[k] = g_rel * 32u + 8u * (uint32_t)l.r4;
+    }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
-    const bool on = t.live && i < t.c.valid_rpw;
-    const size_t rt = (size_t)(t.c.rt_first + i);
-    const auto br = make_rsrc(p.bits + ((size_t)t.kt * p.RT + rt) * kTileBytes, on ? kTileBytes : 0u);
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      T.bw[i][q] = load16(br, (uint32_t)(q * kChunkTile * kRowTile) + l.block);
+    const bool on = i < nrt;
     // scale block of (row tile, group): [plane][16 rows] fp16; this lane's four
     // rows of plane q are 8 bytes at q*32 + 8*r4
-    const auto ar = make_rsrc(p.alpha + (rt * p.G + g_first) * (8 * Q), on ? g_span * 32u * Q : 0u);
+    const uint32_t blk = (uint32_t)(t.c.rt_first + i) * (uint32_t)p.G + (uint32_t)g_first;
+    const auto ar = make_rsrc(p.alpha, on ? (blk + g_span) * (32u * Q) : 0u);
 #pragma unroll
-    for (int k = 0; k < (GQ ? 1 : 4); ++k) {
+    for (int k = 0; k < NV; ++k) {
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const uint2 v = load8(ar, g_rel[k] * 32u * Q + (uint32_t)(q * 32 + 8 * l.r4));
+        const uint2 v = load8(ar, aoff[k] + (uint32_t)(q * 32), blk * (32u * Q));
         T.aw[i][(k * Q + q) * 2] = v.x;
         T.aw[i][(k * Q + q) * 2 + 1] = v.y;
       }
     }
     if constexpr (OFF) {
-      const auto orr = make_rsrc(p.offset + (rt * p.G + g_first) * 8, on ? g_span * 32u : 0u);
+      const auto orr = make_rsrc(p.offset, on ? (blk + g_span) * 32u : 0u);
 #pragma unroll
-      for (int k = 0; k < (GQ ? 1 : 4); ++k) {
-        const uint2 v = load8(orr, g_rel[k] * 32u + (uint32_t)(8 * l.r4));
+      for (int k = 0; k < NV; ++k) {
+        const uint2 v = load8(orr, ooff[k], blk * 32u);
         T.ow[i][2 * k] = v.x;
         T.ow[i][2 * k + 1] = v.y;
       }
@@ -481,7 +523,8 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   __shared__ float lut[2 * kLutWords];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
 
-  const LaneCtx l = lane_ctx();
+  LaneCtx l = lane_ctx();
+  if constexpr (GQ) tile_group_offsets<Q>(p, l);
 
   float acc[MC][RPW][4];
 #pragma unroll
@@ -545,7 +588,7 @@ using KernelFn = void (*)(Params);
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int NR>
 constexpr int kVgprEstimate =
     NR * (RPW * Q * 4 + RPW * (GQ ? 2 * Q : 8 * Q) + MC * 4 + (OFF ? RPW * (GQ ? 2 : 8) : 0)) +
-    4 * RPW * MC + (GQ ? 16 : 4) + 32;   // + the table entries of one lookup group in flight
+    4 * RPW * MC + (GQ ? 16 + 2 : 4) + 32;   // + the table entries of one lookup group in flight (+ lane scale offsets)
 
 template <int W>
 constexpr int kBudget = W == 16 ? 128 : 256;

@@ -261,3 +261,9 @@ def test_run_validates_before_any_hip_call():
     assert run(big, 1, ws=None, wsb=0) == 1
     assert run(big, 1, ws=A, wsb=need - 1) == 4
     assert run(big, 1, ws=A + 4, wsb=need) == 5
+    # each input buffer must be under 4 GiB (32-bit offsets in the kernel)
+    huge_bits = lg.Shape(1 << 20, 1 << 13, 8, 128, 0)      # 8 GiB of sign planes
+    assert run(huge_bits, 1) == 2
+    assert L.lutgemm_workspace_size(ctypes.byref(huge_bits), 1, ctypes.byref(ctypes.c_size_t())) == 2
+    wide = lg.Shape(64, 1 << 16, 1, 128, 0)
+    assert run(wide, 32768) == 2                           # x of exactly 4 GiB: rejected
