@@ -93,8 +93,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed launches first (the clocks take a few hundred to settle)")
+    ap.add_argument("--warmup", type=int, default=20000,
+                    help="untimed launches first (about a second: the clocks take that long to settle)")
     ap.add_argument("--workload", default="opt175b_ffn_up")
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct weight copies cycled through (0: enough for >= 1 GiB)")

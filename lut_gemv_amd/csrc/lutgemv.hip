@@ -30,17 +30,18 @@ __global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
 
 // ------------------------------------------------------------------ dispatch
 
-// ring: 3 asks for the 3-deep ring where an instance has one, 0 for the default.
-KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring) {
+// ring: >= 3 asks for the deeper ring where an instance has one, 0 for the
+// default; xl: the variant with x staged in LDS (batch 1).
+KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring, bool xl) {
   switch (q) {
-    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring);
-    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring);
-    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring);
-    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring);
-    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring);
-    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring);
-    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring);
-    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring);
+    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl);
+    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl);
+    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring, xl);
+    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring, xl);
+    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring, xl);
+    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring, xl);
+    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring, xl);
+    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring, xl);
     default: return nullptr;
   }
 }
@@ -48,22 +49,25 @@ KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring)
 struct Config {
   int RPW, MC, S, W;
   int RI;                // row tiles per row block (<= W * RPW)
-  int ring;              // 3: the 3-deep ring; 0: the instance's default
+  int ring;              // >= 3: the deeper ring; 0: the instance's default
+  bool xl;               // x staged in LDS
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
 };
 
 struct TileOverride {
-  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0;
+  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1;
 };
 
-// Optional tuning override "RPW,S[,W[,MC[,ring[,RI]]]]" (LUTGEMM_TILE); never
-// needed for correctness.
+// Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL]]]]]" (LUTGEMM_TILE);
+// never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
+// (default: where possible).
 bool tile_override(TileOverride* o) {
   const char* e = getenv("LUTGEMM_TILE");
   if (!e || !*e) return false;
-  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring, &o->ri);
+  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring,
+                       &o->ri, &o->xl);
   return n >= 2;
 }
 
@@ -75,7 +79,8 @@ bool tile_override(TileOverride* o) {
 // Batch 1 with grouped scales (the HBM-bound case): when the matrix has
 // between 8 and 16 row tiles per CU, each CU takes one row block of
 // ceil(row tiles / CUs) row tiles over the whole input dimension, with 16
-// waves and a 3-deep ring. All CUs then stream the same input tile window in
+// waves, x staged in LDS and a 2-deep ring (or, when x does not fit, x from
+// L2 and a 3-deep ring). All CUs then stream the same input tile window in
 // step (the best access pattern measured), with no split reduction.
 //
 // Otherwise a cost estimate charges each item its tiles, weighted by the row
@@ -87,16 +92,23 @@ Config choose_config(const Geometry& G, int64_t m) {
   c.gq = (G.g % 32) == 0;
   c.W = 0;   // stays 0 if no instance fits (reported as an internal error)
   c.ring = 0;
+  c.xl = false;
   const int q = (int)G.q;
   const bool off = G.has_offset;
+  // batch 1 with x small enough: stage it in LDS (16-wave instances)
+  const bool xl_ok = m == 1 && G.KT * kChunkTile <= kXChunks;
   const int64_t ri1 = (G.RT + kCUs - 1) / kCUs;
-  if (m == 1 && c.gq && ri1 >= 8 && ri1 <= 16 && pick_kernel(q, 1, 1, true, off, 16, 3) &&
-      pick_kernel(q, 1, 1, true, off, 16, 3) != pick_kernel(q, 1, 1, true, off, 16, 0)) {
+  // x in LDS with the 2-deep ring, else the 3-deep ring with x from L2
+  const bool xl1 = xl_ok && pick_kernel(q, 1, 1, true, off, 16, 0, true) != nullptr;
+  const KernelFn deep = pick_kernel(q, 1, 1, true, off, 16, 3, false);
+  const bool has_deep = deep && deep != pick_kernel(q, 1, 1, true, off, 16, 0, false);
+  if (m == 1 && c.gq && ri1 >= 8 && ri1 <= 16 && (xl1 || has_deep)) {
     c.W = 16;
     c.RPW = 1;
     c.MC = 1;
     c.RI = (int)ri1;
-    c.ring = 3;
+    c.ring = xl1 ? 0 : 3;
+    c.xl = xl1;
     c.n_rb = (G.RT + ri1 - 1) / ri1;
     c.n_bg = 1;
     c.S = 1;
@@ -107,7 +119,7 @@ Config choose_config(const Geometry& G, int64_t m) {
                           {8, 2, 2, 1.3}, {8, 1, 2, 1.3}, {8, 2, 1, 1.3}, {8, 1, 1, 1.3}};
     for (const Cand& v : cands) {
       if (v.mc > 1 && m < v.mc) continue;
-      if (!pick_kernel(q, v.rpw, v.mc, c.gq, off, v.w, 0)) continue;
+      if (!pick_kernel(q, v.rpw, v.mc, c.gq, off, v.w, 0, false)) continue;
       const int64_t rows = (int64_t)v.w * v.rpw;            // row tiles per item
       const int64_t n_rb = (G.RT + rows - 1) / rows;
       const int64_t n_bg = (m + v.mc - 1) / v.mc;
@@ -130,16 +142,20 @@ Config choose_config(const Geometry& G, int64_t m) {
         }
       }
     }
+    c.xl = xl_ok && pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, 0, true) != nullptr;
   }
   TileOverride o;
   if (tile_override(&o)) {
     const int w = o.w ? o.w : c.W;
     const int mc = o.mc ? o.mc : c.MC;
-    if (pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring)) {
+    const bool xl = o.xl < 0 ? xl_ok && pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, true)
+                             : (o.xl > 0 && xl_ok);
+    if (pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, xl)) {
       c.W = w;
       c.RPW = o.rpw;
       c.MC = mc;
       c.ring = o.ring;
+      c.xl = xl;
       c.RI = (o.ri >= 1 && o.ri <= c.W * c.RPW) ? o.ri : c.W * c.RPW;
       c.n_rb = (G.RT + c.RI - 1) / c.RI;
       c.n_bg = (m + c.MC - 1) / c.MC;
@@ -247,7 +263,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
       return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
     }
 
-    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring);
+    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl);
     if (!fn) return LUTGEMM_ERR_INTERNAL;
     Params p{};
     p.bits = (const uint8_t*)d_bits;

@@ -48,6 +48,9 @@
 namespace lutgemm {
 
 constexpr int kLutWords = 256 * kChunkTile;   // one table tile: 64 KiB of fp32 entries
+// At batch 1 the whole of x can be staged in LDS next to the two tables (128 KiB):
+// up to 1920 chunks of 8 inputs (30 KiB), i.e. K <= 15360.
+constexpr int kXChunks = 1920;
 constexpr int kCUs = 256;                     // MI355X compute units (dispatch heuristic)
 // Split reductions keep their arrival counters in a fixed region at the start
 // of the workspace, so any later call finds its counters zero whatever its shape.
@@ -225,7 +228,7 @@ __device__ __forceinline__ void tile_group_offsets(const Params& p, LaneCtx& l) 
 // Issue the loads of the tile at T.pos (all of them unconditional; activations
 // first, so the table build waits only for those). A dead position gives
 // zero-length ranges: the instructions issue but touch no memory.
-template <int Q, int RPW, int MC, bool GQ, bool OFF>
+template <int Q, int RPW, int MC, bool GQ, bool OFF, bool XL>
 __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
                                           TileRegs<Q, RPW, MC, GQ, OFF>& T) {
   constexpr uint32_t kTileBytes = Q * kChunkTile * kRowTile;
@@ -236,11 +239,13 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
   // bytes for this wave; the tile's position goes in the scalar offset (each
   // buffer is under 4 GiB). A dead position is an empty range.
   const uint32_t kin = t.live ? (uint32_t)min(kChunkTile * 8, p.K - k0) : 0u;
+  if constexpr (!XL) {   // (with XL the activations are in LDS)
 #pragma unroll
-  for (int r = 0; r < MC; ++r) {
-    const uint32_t nb = (r < t.c.rows_here) ? kin * 2u : 0u;
-    const uint32_t xs = ((uint32_t)(t.c.r0 + r) * (uint32_t)p.K + (uint32_t)k0) * 2u;
-    T.xv[r] = load16(make_rsrc(p.x, nb ? xs + nb : 0u), (uint32_t)l.lane * 16u, xs);
+    for (int r = 0; r < MC; ++r) {
+      const uint32_t nb = (r < t.c.rows_here) ? kin * 2u : 0u;
+      const uint32_t xs = ((uint32_t)(t.c.r0 + r) * (uint32_t)p.K + (uint32_t)k0) * 2u;
+      T.xv[r] = load16(make_rsrc(p.x, nb ? xs + nb : 0u), (uint32_t)l.lane * 16u, xs);
+    }
   }
   // sign blocks of this wave's row tiles (adjacent in the input-tile-first order)
   const int nrt = t.live ? t.c.nrt : 0;
@@ -514,13 +519,18 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // step's table in the other LDS buffer, and ends at the step's one barrier.
 // Q: sign planes; RPW: row tiles per wave; MC: batch rows per item; GQ: see
 // TileRegs; OFF: offset term; W: waves per workgroup (8, 12 or 16).
-template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR>
+// XL (batch 1 only): x is staged whole in LDS at the start, and the tables are
+// built from there, instead of every wave loading each x tile from L2 (all
+// waves of all CUs reading the same lines).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL>
 // The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
 // also the most that can ever run; saying so lets the scheduler use the
 // whole register budget to keep table lookups in flight.
 __global__ void __launch_bounds__(W * 64, W / 4)
     __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) lutgemv_kernel(Params p) {
+  static_assert(!XL || MC == 1, "x in LDS is for batch 1");
   __shared__ float lut[2 * kLutWords];
+  __shared__ uint4 xs[XL ? kXChunks : 1];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
 
   LaneCtx l = lane_ctx();
@@ -537,14 +547,29 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   TR R[NR];
   R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
   if (!R[0].pos.live) return;
-  load_tile(p, l, R[0]);
+  load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[0]);
 #pragma unroll
   for (int s = 1; s + 1 < NR; ++s) {
     R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
-    load_tile(p, l, R[s]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[s]);
   }
+  if constexpr (XL) {   // chunk c of x at xs[c]; zero past the end of x
+    const uint4* xg = reinterpret_cast<const uint4*>(p.x);
+    const int C = p.K / 8;
+    for (int c = (int)threadIdx.x; c < p.KT * kChunkTile; c += W * 64)
+      xs[c] = c < C ? xg[c] : uint4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+  // activations of chunk `lane` of a tile, for the table build
+  auto xtile = [&](const TR& T, int r) -> uint4 {
+    if constexpr (XL) {
+      return xs[T.pos.kt * kChunkTile + l.lane];
+    } else {
+      return T.xv[r];
+    }
+  };
   int buf = 0;
-  build_table<W>(lut, 0, l, R[0].xv[0]);
+  build_table<W>(lut, 0, l, xtile(R[0], 0));
   __syncthreads();
   bool done = false;
   while (!done) {
@@ -555,15 +580,15 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         TR& nxt = R[(s + 1) % NR];
         TR& pre = R[(s + NR - 1) % NR];
         pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
-        load_tile(p, l, pre);
+        load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, pre);
 #pragma unroll
         for (int r = 0; r < MC; ++r) {
           if (r < cur.pos.c.rows_here) {  // uniform over the workgroup
             lookups(l, r, buf, lut, cur, acc);
             if (r + 1 < cur.pos.c.rows_here) {
-              build_table<W>(lut, buf ^ 1, l, cur.xv[r + 1]);
+              build_table<W>(lut, buf ^ 1, l, xtile(cur, r + 1 < MC ? r + 1 : r));
             } else if (nxt.pos.live) {
-              build_table<W>(lut, buf ^ 1, l, nxt.xv[0]);
+              build_table<W>(lut, buf ^ 1, l, xtile(nxt, 0));
             }
             __syncthreads();
             buf ^= 1;
@@ -584,11 +609,13 @@ using KernelFn = void (*)(Params);
 // Register budget per wave: 256 VGPRs with 8 waves (two per SIMD), 128 with 16
 // (four per SIMD). An instance keeps a ring of NR tiles in flight, the
 // accumulators and some temporaries in that budget: three tiles when they fit,
-// else two (16 waves always use two).
-template <int Q, int RPW, int MC, bool GQ, bool OFF, int NR>
+// else two (16 waves use two, plus a deeper ring where it fits).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int NR, bool XL = false>
 constexpr int kVgprEstimate =
-    NR * (RPW * Q * 4 + RPW * (GQ ? 2 * Q : 8 * Q) + MC * 4 + (OFF ? RPW * (GQ ? 2 : 8) : 0)) +
-    4 * RPW * MC + (GQ ? 16 + 2 : 4) + 32;   // + the table entries of one lookup group in flight (+ lane scale offsets)
+    NR * (RPW * Q * 4 + RPW * (GQ ? 2 * Q : 8 * Q) + (XL ? 0 : MC * 4) +
+          (OFF ? RPW * (GQ ? 2 : 8) : 0)) +
+    4 * RPW * MC + (GQ ? 16 + 2 : 4) + 32;   // + the table entries of one lookup group in
+                                             // flight (+ lane scale offsets)
 
 template <int W>
 constexpr int kBudget = W == 16 ? 128 : 256;
@@ -602,66 +629,81 @@ constexpr bool kInstantiated =
     (W == 16 ? (MC == 1 && GQ) : (W == 8)) &&
     kVgprEstimate<Q, RPW, MC, GQ, OFF, kRing<Q, RPW, MC, GQ, OFF, W>> <= kBudget<W>;
 
-// A deeper ring with 16 waves, when it fits (kept selectable for tuning).
-template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
-constexpr bool kDeep16 =
-    W == 16 && MC == 1 && GQ && kVgprEstimate<Q, RPW, MC, GQ, OFF, 3> <= kBudget<W>;
+// Whether a 16-wave instance with an NR-deep ring fits the register budget.
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, bool XL, int NR>
+constexpr bool kFits16 =
+    W == 16 && MC == 1 && GQ && kVgprEstimate<Q, RPW, MC, GQ, OFF, NR, XL> <= kBudget<W>;
 
-// ring: 3 selects the deeper ring where an instance has one (tuning), else 0.
+// ring 3 or 4 selects a deeper ring where an instance has one (16 waves); xl
+// the x-in-LDS variant (16 waves, batch 1, grouped scales).
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
-KernelFn kernel_or_null(int ring) {
+KernelFn kernel_or_null(int ring, bool xl) {
   if constexpr (kInstantiated<Q, RPW, MC, GQ, OFF, W>) {
-    if constexpr (kDeep16<Q, RPW, MC, GQ, OFF, W>) {
-      if (ring == 3) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3>;
+    if constexpr (W == 16 && MC == 1 && GQ) {
+      if (xl) {
+        if constexpr (kFits16<Q, RPW, MC, GQ, OFF, W, true, 4>) {
+          if (ring == 4) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 4, true>;
+        }
+        if constexpr (kFits16<Q, RPW, MC, GQ, OFF, W, true, 3>) {
+          if (ring >= 3) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3, true>;
+        }
+        return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 2, true>;
+      }
+      if constexpr (kFits16<Q, RPW, MC, GQ, OFF, W, false, 3>) {
+        if (ring >= 3) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3, false>;
+      }
     }
-    return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRing<Q, RPW, MC, GQ, OFF, W>>;
+    if (xl) return nullptr;
+    return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRing<Q, RPW, MC, GQ, OFF, W>, false>;
   } else {
     (void)ring;
+    (void)xl;
     return nullptr;
   }
 }
 
 template <int Q, int RPW, int MC, int W>
-KernelFn pick_flags(bool gq, bool off, int ring) {
+KernelFn pick_flags(bool gq, bool off, int ring, bool xl) {
   if (gq)
-    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring)
-               : kernel_or_null<Q, RPW, MC, true, false, W>(ring);
-  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring)
-             : kernel_or_null<Q, RPW, MC, false, false, W>(ring);
+    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl)
+               : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl);
+  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring, xl)
+             : kernel_or_null<Q, RPW, MC, false, false, W>(ring, xl);
 }
 
 template <int Q, int W>
-KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring) {
+KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl) {
   if (mc == 1) {
-    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring);
-    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring);
+    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl);
+    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring, xl);
   } else if (mc == 2) {
-    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring);
-    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring);
+    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring, xl);
+    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring, xl);
   } else if (mc == 4) {
-    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring);
-    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring);
+    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring, xl);
+    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring, xl);
   }
   return nullptr;
 }
 
 // The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
-// item, scale groups aligned to 32 inputs (gq), an offset term (off) and w
-// waves per workgroup, or nullptr if none is built.
+// item, scale groups aligned to 32 inputs (gq), an offset term (off), w waves
+// per workgroup, ring depth (0 default, >= 3 deeper) and x in LDS (xl), or
+// nullptr if none is built.
 template <int Q>
-KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring) {
-  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring);
-  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring);
+KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl) {
+  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl);
+  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl);
   return nullptr;
 }
 
-extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int);
-extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int);
-extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int);
-extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int);
-extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int);
-extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int);
-extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int);
-extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int);
+extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool);
 
 }  // namespace lutgemm
