@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20000,
                     help="untimed launches first (about a second: the clocks take that long to settle)")
     ap.add_argument("--workload", default="opt175b_ffn_up")
+    ap.add_argument("--kernel", choices=["lut", "dequant"], default="lut",
+                    help="lut: the LUT-GEMV (the product); dequant: the dequantizing comparison "
+                         "kernel on the same packed data")
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct weight copies cycled through (0: enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -148,10 +151,15 @@ def main():
     args_c = [(c.shape, c.d_bits.data_ptr(), c.d_alpha.data_ptr(),
                c.d_offset.data_ptr() if has_off else None) for c in copies]
 
-    def launch(k):
-        shape, b, a, o = args_c[k % R]
-        lg.lutgemm_run(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(),
-                       ws.data_ptr() if ws_bytes else None, ws_bytes, sh)
+    if args.kernel == "lut":
+        def launch(k):
+            shape, b, a, o = args_c[k % R]
+            lg.lutgemm_run(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(),
+                           ws.data_ptr() if ws_bytes else None, ws_bytes, sh)
+    else:
+        def launch(k):
+            shape, b, a, o = args_c[k % R]
+            lg.bcq_dequant_gemv(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(), sh)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -199,7 +207,7 @@ def main():
     ms_per_step = t_total * 1e3 / K_steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / avg_kernel_s / 1e9
-    traffic = stored_traffic()
+    traffic = stored_traffic() if args.kernel == "lut" else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -212,7 +220,8 @@ def main():
         log(f"cpu baseline: {cpu['sample']}")
 
     out = {
-        "metric": METRIC if w.name == "opt175b_ffn_up" else f"us/GEMV + achieved HBM GB/s, {w.name}",
+        "metric": (METRIC if w.name == "opt175b_ffn_up" and args.kernel == "lut"
+                   else f"us/GEMV + achieved HBM GB/s, {w.name}, {args.kernel} kernel"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -227,7 +236,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "N": w.N, "K": w.K, "q": w.q, "g": w.g, "m": w.m,
+        "config": {"workload": w.name, "kernel": args.kernel,
+                   "N": w.N, "K": w.K, "q": w.q, "g": w.g, "m": w.m,
                    "offset": bool(has_off), "x": "fp16", "y": "fp16",
                    "rotating_copies": R, "algorithmic_bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

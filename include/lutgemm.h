@@ -155,6 +155,20 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits,
                 void* d_y, void* d_workspace, size_t workspace_bytes,
                 void* stream);
 
+/* The comparison point, not the method: y = W_hat x by expanding every weight
+ * to fp16 (W_hat[j][k] = sum_i +-alpha[i][j][k/g] (+ offset), packed fp16 adds)
+ * and taking fp16 dot products with fp32 accumulation, the way dequantizing
+ * weight-only kernels work (Elamur card "LUT-GEMM -- paper by Park et al.
+ * (2022)", section "Summary": LUT-GEMM is set against kernels that expand
+ * low-bit weights to FP16 before multiplying). Same arguments, packed format,
+ * alignment rules and status codes as lutgemm_run, without a workspace; y is
+ * within the same tolerance of the exact product (the weight sums are rounded
+ * to fp16). Asynchronous on `stream`; all argument checks run before any HIP
+ * call. */
+int bcq_dequant_gemv(const lutgemm_shape* s, int32_t m, const void* d_bits,
+                     const void* d_alpha, const void* d_offset, const void* d_x,
+                     void* d_y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

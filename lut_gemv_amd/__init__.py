@@ -20,7 +20,7 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "LutGemmError", "Shape", "lib", "abi_version", "status_string",
     "check_shape", "packed_sizes", "workspace_size", "workspace_init",
-    "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "PackedBCQ", "STATUS",
+    "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "PackedBCQ", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.bcq_pack_uniform.argtypes = [_SHP, _P, _P, _P, _P, _SZ, _P, _SZ, _P, _SZ, _SZP]
     L.lutgemm_run.restype = ctypes.c_int
     L.lutgemm_run.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    L.bcq_dequant_gemv.restype = ctypes.c_int
+    L.bcq_dequant_gemv.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
     _LIB = L
     return L
 
@@ -204,6 +206,13 @@ def lutgemm_run(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: Optio
                              d_workspace, int(workspace_bytes), stream), "lutgemm_run")
 
 
+def bcq_dequant_gemv(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: Optional[int],
+                     d_x: int, d_y: int, stream: Optional[int]):
+    """Raw entry point of the dequantizing comparison kernel (same packed format)."""
+    _check(lib().bcq_dequant_gemv(ctypes.byref(shape), int(m), d_bits, d_alpha, d_offset, d_x,
+                                  d_y, stream), "bcq_dequant_gemv")
+
+
 class PackedBCQ:
     """A packed BCQ weight in device memory, ready for :meth:`__call__`.
 
@@ -268,4 +277,19 @@ class PackedBCQ:
                     self.d_offset.data_ptr() if self.d_offset is not None else None,
                     x.data_ptr(), out.data_ptr(),
                     ws.data_ptr() if ws is not None else None, ws_bytes, stream)
+        return out
+
+    def dequant(self, x, out=None):
+        """The same product by the dequantizing comparison kernel (bcq_dequant_gemv)."""
+        import torch
+        if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != self.K:
+            raise ValueError(f"x must be fp16 [m][{self.K}]")
+        x = x.contiguous()
+        m = x.shape[0]
+        if out is None:
+            out = torch.empty((m, self.N), dtype=torch.float16, device=x.device)
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        bcq_dequant_gemv(self.shape, m, self.d_bits.data_ptr(), self.d_alpha.data_ptr(),
+                         self.d_offset.data_ptr() if self.d_offset is not None else None,
+                         x.data_ptr(), out.data_ptr(), stream)
         return out

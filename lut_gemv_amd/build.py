@@ -67,11 +67,14 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     incs = [f"-I{INCLUDE}", f"-I{CSRC}"]
     tmp = tempfile.mkdtemp(prefix="lutgemm_build_")
     try:
-        objs = [os.path.join(tmp, "pack.o"), os.path.join(tmp, "lutgemv.o")]
+        objs = [os.path.join(tmp, "pack.o"), os.path.join(tmp, "lutgemv.o"),
+                os.path.join(tmp, "dequant.o")]
         jobs = [
             [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "pack.cpp"), "-o", objs[0]],
             [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c",
              os.path.join(CSRC, "lutgemv.hip"), "-o", objs[1]],
+            [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c", "-Rpass-analysis=kernel-resource-usage",
+             os.path.join(CSRC, "dequant.hip"), "-o", objs[2]],
         ]
         # the kernel instances of each plane count q build in their own unit
         for q in range(1, 9):

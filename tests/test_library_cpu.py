@@ -267,3 +267,23 @@ def test_run_validates_before_any_hip_call():
     assert L.lutgemm_workspace_size(ctypes.byref(huge_bits), 1, ctypes.byref(ctypes.c_size_t())) == 2
     wide = lg.Shape(64, 1 << 16, 1, 128, 0)
     assert run(wide, 32768) == 2                           # x of exactly 4 GiB: rejected
+
+
+def test_dequant_validates_before_any_hip_call():
+    """The dequantizing comparison kernel reports argument errors without the GPU."""
+    L = lg.lib()
+    ok = lg.Shape(64, 512, 3, 128, 0)
+    A = 0x100000
+    def run(shape, m, b=A, a=A, o=None, x=A, y=A):
+        return L.bcq_dequant_gemv(ctypes.byref(shape) if shape is not None else None, m, b, a,
+                                  o, x, y, None)
+    assert run(None, 1) == 1
+    assert run(lg.Shape(64, 12, 3, 128, 0), 1) == 2
+    assert run(ok, -1) == 2
+    assert run(ok, 0) == 0
+    assert run(ok, 1, y=None) == 1
+    assert run(ok, 1, b=None) == 1
+    assert run(lg.Shape(64, 512, 3, 128, 1), 1, o=None) == 1
+    assert run(ok, 1, b=A + 8) == 5
+    assert run(ok, 1, x=A + 2) == 5
+    assert run(ok, 1, a=A + 2) == 5
