@@ -155,6 +155,23 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits,
                 void* d_y, void* d_workspace, size_t workspace_bytes,
                 void* stream);
 
+/* Storage in bits of the matrix of shape *s: q sign bits per weight, one fp16
+ * scale per (plane, row, group of g) and one fp16 offset per (row, group) when
+ * s->has_offset (Elamur card, section "Interesting ideas: Group size as a
+ * separate hyper-parameter": scales count toward the storage). Host only. */
+int bcq_footprint_bits(const lutgemm_shape* s, uint64_t* bits);
+
+/* Group sizes for a storage target (same card section: q and g are chosen
+ * together for a target compression). For each plane count q = 1..8, the
+ * smallest g (a divisor of K, multiple of 8: the finest scales) whose footprint
+ * for an N x K matrix is at most max_bits_per_weight * N * K bits:
+ * out_g[q-1] = g and out_bits[q-1] = the footprint, or both 0 when no g fits.
+ * out_g and out_bits hold 8 entries each. Errors: LUTGEMM_ERR_NULL,
+ * LUTGEMM_ERR_SHAPE (N < 1, K < 8, K % 8, N or K >= 2^30, has_offset not 0/1),
+ * LUTGEMM_ERR_VALUE (target not in (0, 1e6]). Host only. */
+int bcq_search_group_sizes(int64_t N, int64_t K, int32_t has_offset, double max_bits_per_weight,
+                           int32_t* out_g, uint64_t* out_bits);
+
 /* The comparison point, not the method: y = W_hat x by expanding every weight
  * to fp16 (W_hat[j][k] = sum_i +-alpha[i][j][k/g] (+ offset), packed fp16 adds)
  * and taking fp16 dot products with fp32 accumulation, the way dequantizing

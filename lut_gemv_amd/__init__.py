@@ -20,7 +20,8 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "LutGemmError", "Shape", "lib", "abi_version", "status_string",
     "check_shape", "packed_sizes", "workspace_size", "workspace_init",
-    "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "PackedBCQ", "STATUS",
+    "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "footprint_bits",
+    "search_group_sizes", "PackedBCQ", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +86,12 @@ def lib() -> ctypes.CDLL:
     L.bcq_pack_uniform.argtypes = [_SHP, _P, _P, _P, _P, _SZ, _P, _SZ, _P, _SZ, _SZP]
     L.lutgemm_run.restype = ctypes.c_int
     L.lutgemm_run.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    L.bcq_footprint_bits.restype = ctypes.c_int
+    L.bcq_footprint_bits.argtypes = [_SHP, ctypes.POINTER(ctypes.c_uint64)]
+    L.bcq_search_group_sizes.restype = ctypes.c_int
+    L.bcq_search_group_sizes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_double, ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_uint64)]
     L.bcq_dequant_gemv.restype = ctypes.c_int
     L.bcq_dequant_gemv.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
     _LIB = L
@@ -204,6 +211,25 @@ def lutgemm_run(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: Optio
     """Raw entry point: device addresses as integers, ``stream`` a hipStream_t handle."""
     _check(lib().lutgemm_run(ctypes.byref(shape), int(m), d_bits, d_alpha, d_offset, d_x, d_y,
                              d_workspace, int(workspace_bytes), stream), "lutgemm_run")
+
+
+def footprint_bits(N: int, K: int, q: int, g: int, has_offset: bool = False) -> int:
+    """Storage in bits of an N x K BCQ matrix, scales (and offsets) included."""
+    out = ctypes.c_uint64()
+    _check(lib().bcq_footprint_bits(ctypes.byref(_shape(N, K, q, g, has_offset)), ctypes.byref(out)),
+           "bcq_footprint_bits")
+    return out.value
+
+
+def search_group_sizes(N: int, K: int, max_bits_per_weight: float, has_offset: bool = False):
+    """{q: (g, bits)} for q = 1..8: the finest group size meeting the storage target
+    (q absent when none does)."""
+    gs = (ctypes.c_int32 * 8)()
+    bs = (ctypes.c_uint64 * 8)()
+    _check(lib().bcq_search_group_sizes(int(N), int(K), int(bool(has_offset)),
+                                        float(max_bits_per_weight), gs, bs),
+           "bcq_search_group_sizes")
+    return {q + 1: (gs[q], bs[q]) for q in range(8) if gs[q]}
 
 
 def bcq_dequant_gemv(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: Optional[int],

@@ -68,9 +68,10 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     tmp = tempfile.mkdtemp(prefix="lutgemm_build_")
     try:
         objs = [os.path.join(tmp, "pack.o"), os.path.join(tmp, "lutgemv.o"),
-                os.path.join(tmp, "dequant.o")]
+                os.path.join(tmp, "dequant.o"), os.path.join(tmp, "footprint.o")]
         jobs = [
             [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "pack.cpp"), "-o", objs[0]],
+            [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "footprint.cpp"), "-o", objs[3]],
             [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c",
              os.path.join(CSRC, "lutgemv.hip"), "-o", objs[1]],
             [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c", "-Rpass-analysis=kernel-resource-usage",

@@ -56,6 +56,7 @@ __all__ = [
     "parity_ok",
     "ROW_TILE",
     "CHUNK_TILE",
+    "search_group_sizes",
 ]
 
 # Packed-layout tile sizes of this project's device format (see :func:`pack`).
@@ -243,6 +244,23 @@ def footprint_bits(n: int, q: int, g: int, offset: bool = False) -> int:
     Group size as a separate hyper-parameter") asks."""
     groups = -(-n // g)
     return q * n + 16 * q * groups + (16 * groups if offset else 0)
+
+
+def search_group_sizes(N: int, K: int, max_bits_per_weight: float, has_offset: bool = False):
+    """For each q = 1..8 the finest admissible group size (g a divisor of K and a
+    multiple of 8) whose storage, by :func:`footprint_bits`, is within the target
+    of bits per weight; {q: (g, bits)}, q absent when no g fits. Plain
+    enumeration of every (q, g) pair (card section "Interesting ideas: Group size
+    as a separate hyper-parameter": q and g are searched jointly for a target
+    compression)."""
+    n = N * K
+    out = {}
+    for q in range(1, 9):
+        fits = [(g, footprint_bits(n, q, g, has_offset)) for g in range(8, K + 1, 8)
+                if K % g == 0 and footprint_bits(n, q, g, has_offset) <= max_bits_per_weight * n]
+        if fits:
+            out[q] = min(fits)
+    return out
 
 
 def packed_sizes(N: int, K: int, q: int, g: int, has_offset: bool):

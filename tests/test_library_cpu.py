@@ -287,3 +287,28 @@ def test_dequant_validates_before_any_hip_call():
     assert run(ok, 1, b=A + 8) == 5
     assert run(ok, 1, x=A + 2) == 5
     assert run(ok, 1, a=A + 2) == 5
+
+
+@pytest.mark.parametrize("N,K,q,g,off", [(49152, 12288, 3, 128, False), (11008, 4096, 4, 128, True),
+                                         (1, 8, 8, 8, True), (7, 520, 2, 40, False)])
+def test_footprint_matches_oracle(N, K, q, g, off):
+    assert lg.footprint_bits(N, K, q, g, off) == oracle.footprint_bits(N * K, q, g, off)
+
+
+@pytest.mark.parametrize("N,K,bpw,off", [(49152, 12288, 3.25, False), (11008, 4096, 4.5, True),
+                                         (28672, 8192, 2.125, False), (3, 1000, 9.0, True),
+                                         (5, 24, 1.0, False), (64, 4096, 8.0 + 1 / 3, True)])
+def test_group_search_matches_oracle(N, K, bpw, off):
+    assert lg.search_group_sizes(N, K, bpw, off) == oracle.search_group_sizes(N, K, bpw, off)
+
+
+def test_group_search_errors():
+    L = lg.lib()
+    g = (ctypes.c_int32 * 8)()
+    b = (ctypes.c_uint64 * 8)()
+    assert L.bcq_search_group_sizes(0, 512, 0, 3.0, g, b) == 2
+    assert L.bcq_search_group_sizes(4, 12, 0, 3.0, g, b) == 2
+    assert L.bcq_search_group_sizes(4, 512, 2, 3.0, g, b) == 2
+    assert L.bcq_search_group_sizes(4, 512, 0, 0.0, g, b) == 3
+    assert L.bcq_search_group_sizes(4, 512, 0, float("nan"), g, b) == 3
+    assert L.bcq_search_group_sizes(4, 512, 0, 3.0, None, b) == 1

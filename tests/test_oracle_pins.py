@@ -477,3 +477,15 @@ def test_planted_mistakes(monkeypatch, name, mutant):
     monkeypatch.setattr(ob, name, mutant)
     with pytest.raises(AssertionError):
         _run_pins()
+
+
+def test_group_search_golden():
+    """The oracle's (q, g) search against hand-worked cases (bits per weight)."""
+    fx = load_golden("group_search_example.json")
+    for c in fx["cases"]:
+        got = ob.search_group_sizes(c["N"], c["K"], c["bpw"], c["offset"])
+        want = {int(q): (g, bpw) for q, (g, bpw) in c["expect"].items()}
+        assert sorted(got) == sorted(want)
+        for q, (g, bpw) in want.items():
+            assert got[q][0] == g
+            assert got[q][1] == bpw * c["N"] * c["K"]
