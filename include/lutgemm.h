@@ -172,6 +172,24 @@ int bcq_footprint_bits(const lutgemm_shape* s, uint64_t* bits);
 int bcq_search_group_sizes(int64_t N, int64_t K, int32_t has_offset, double max_bits_per_weight,
                            int32_t* out_g, uint64_t* out_bits);
 
+/* Binary-coding quantization of an fp16 matrix into the logical BCQ format
+ * that bcq_pack takes (the format of the card's sections "Summary" and
+ * "Interesting ideas: Group size as a separate hyper-parameter"; the pages name
+ * the quantizer only by reference, so the method is this library's reading):
+ * greedy per (row, group): plane by plane, alpha_i = the mean absolute residual
+ * rounded to fp16, b_i = its sign (0 counts as +1); then `iters` rounds of
+ * alternating refinement (least-squares refit of the q scales, rounded to fp16,
+ * kept unchanged when the system is singular or a scale overflows fp16; then each weight
+ * takes its nearest sign combination, lowest index on ties).
+ *   w     fp16 [N][K] (finite)      bits  uint8 [q][N][K/8]  (as for bcq_pack)
+ *   alpha fp16 [q][N][K/g]          *sq_error (may be NULL) = sum (w - W_hat)^2
+ * s->has_offset must be 0; 0 <= iters <= 1000. Errors: LUTGEMM_ERR_SHAPE,
+ * LUTGEMM_ERR_NULL, LUTGEMM_ERR_BUFFER (outputs too small), LUTGEMM_ERR_VALUE
+ * (non-finite w or iters out of range); on error nothing has been written.
+ * Deterministic; host only (CPU threads). */
+int bcq_quantize(const lutgemm_shape* s, const uint16_t* w, int32_t iters, uint8_t* bits,
+                 size_t bits_bytes, uint16_t* alpha, size_t alpha_count, double* sq_error);
+
 /* The comparison point, not the method: y = W_hat x by expanding every weight
  * to fp16 (W_hat[j][k] = sum_i +-alpha[i][j][k/g] (+ offset), packed fp16 adds)
  * and taking fp16 dot products with fp32 accumulation, the way dequantizing

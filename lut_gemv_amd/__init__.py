@@ -21,7 +21,7 @@ __all__ = [
     "LIB_PATH", "LutGemmError", "Shape", "lib", "abi_version", "status_string",
     "check_shape", "packed_sizes", "workspace_size", "workspace_init",
     "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "footprint_bits",
-    "search_group_sizes", "PackedBCQ", "STATUS",
+    "search_group_sizes", "bcq_quantize", "PackedBCQ", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
     L.bcq_search_group_sizes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                          ctypes.c_double, ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_uint64)]
+    L.bcq_quantize.restype = ctypes.c_int
+    L.bcq_quantize.argtypes = [_SHP, _P, ctypes.c_int32, _P, _SZ, _P, _SZ,
+                               ctypes.POINTER(ctypes.c_double)]
     L.bcq_dequant_gemv.restype = ctypes.c_int
     L.bcq_dequant_gemv.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
     _LIB = L
@@ -230,6 +233,19 @@ def search_group_sizes(N: int, K: int, max_bits_per_weight: float, has_offset: b
                                         float(max_bits_per_weight), gs, bs),
            "bcq_search_group_sizes")
     return {q + 1: (gs[q], bs[q]) for q in range(8) if gs[q]}
+
+
+def bcq_quantize(w, q: int, g: int, iters: int = 0):
+    """fp16 W [N][K] -> (bits uint8 [q][N][K/8], alpha fp16 [q][N][K/g], squared error)."""
+    w = np.ascontiguousarray(w, dtype=np.float16)
+    N, K = w.shape
+    bits = np.zeros((q, N, K // 8), np.uint8)
+    alpha = np.zeros((q, N, K // g if K else 0), np.uint16)
+    err = ctypes.c_double()
+    _check(lib().bcq_quantize(ctypes.byref(_shape(N, K, q, g, False)), w.ctypes.data, int(iters),
+                              bits.ctypes.data, bits.nbytes, alpha.ctypes.data, alpha.size,
+                              ctypes.byref(err)), "bcq_quantize")
+    return bits, alpha.view(np.float16), err.value
 
 
 def bcq_dequant_gemv(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: Optional[int],

@@ -32,7 +32,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
-CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread"]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-ffp-contract=off"]
 
 
 def _scratch_users(remarks: str):
@@ -68,10 +68,12 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     tmp = tempfile.mkdtemp(prefix="lutgemm_build_")
     try:
         objs = [os.path.join(tmp, "pack.o"), os.path.join(tmp, "lutgemv.o"),
-                os.path.join(tmp, "dequant.o"), os.path.join(tmp, "footprint.o")]
+                os.path.join(tmp, "dequant.o"), os.path.join(tmp, "footprint.o"),
+                os.path.join(tmp, "quantize.o")]
         jobs = [
             [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "pack.cpp"), "-o", objs[0]],
             [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "footprint.cpp"), "-o", objs[3]],
+            [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "quantize.cpp"), "-o", objs[4]],
             [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c",
              os.path.join(CSRC, "lutgemv.hip"), "-o", objs[1]],
             [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c", "-Rpass-analysis=kernel-resource-usage",

@@ -57,6 +57,7 @@ __all__ = [
     "ROW_TILE",
     "CHUNK_TILE",
     "search_group_sizes",
+    "quantize_bcq",
 ]
 
 # Packed-layout tile sizes of this project's device format (see :func:`pack`).
@@ -244,6 +245,78 @@ def footprint_bits(n: int, q: int, g: int, offset: bool = False) -> int:
     Group size as a separate hyper-parameter") asks."""
     groups = -(-n // g)
     return q * n + 16 * q * groups + (16 * groups if offset else 0)
+
+
+def quantize_bcq(w, q: int, g: int, iters: int = 0):
+    """Binary-coding quantization of an fp16 matrix, step by step (the pages name
+    the quantizer only by reference; this is the reading the design notes give):
+
+    * greedy, per (row, group of g inputs): for plane i = 0..q-1, alpha_i is the
+      mean absolute residual rounded to fp16, b_i is the sign of the residual
+      (+1 for zero), and the residual loses alpha_i * b_i;
+    * then `iters` rounds of: alpha by least squares for the current planes (the
+      normal equations B^T B alpha = B^T w, Gaussian elimination in row order
+      without pivoting, each entry rounded to fp16; a pivot <= 1e-9 g or an fp16
+      overflow keeps the previous alpha), then every weight takes the sign
+      combination whose value is nearest (ties: the lowest combination index, bit
+      i of the index set meaning plane i is +1).
+
+    Returns (bits uint8 [q][N][K/8] in the logical packing, alpha fp16
+    [q][N][K/g], squared error). fp16 inputs make the sums exact in fp64, so the
+    order of summation does not matter here.
+    """
+    w = np.asarray(w, dtype=np.float16)
+    N, K = w.shape
+    G = K // g
+    B = np.zeros((q, N, K), np.int8)
+    A = np.zeros((q, N, G), np.float16)
+    err = 0.0
+    combos = np.array([[1 if (c >> i) & 1 else -1 for i in range(q)] for c in range(1 << q)],
+                      dtype=np.float64)            # [combination][plane]
+    for j in range(N):
+        for t in range(G):
+            wg = w[j, t * g:(t + 1) * g].astype(np.float64)
+            b = np.zeros((q, g))
+            a16 = np.zeros(q, np.float16)
+            r = wg.copy()
+            for i in range(q):
+                a16[i] = np.float16(np.abs(r).sum() / g)
+                b[i] = np.where(r >= 0, 1.0, -1.0)
+                r = r - float(a16[i]) * b[i]
+            for _ in range(iters):
+                M = [[float((b[i] * b[k]).sum()) for k in range(q)] for i in range(q)]
+                v = [float((b[i] * wg).sum()) for i in range(q)]
+                ok = True
+                for c in range(q):
+                    piv = M[c][c]
+                    if not piv > 1e-9 * g:
+                        ok = False
+                        break
+                    for rr in range(c + 1, q):
+                        f = M[rr][c] / piv
+                        for cc in range(c, q):
+                            M[rr][cc] -= f * M[c][cc]
+                        v[rr] -= f * v[c]
+                if ok:
+                    x = [0.0] * q
+                    for c in range(q - 1, -1, -1):
+                        acc = v[c]
+                        for cc in range(c + 1, q):
+                            acc -= M[c][cc] * x[cc]
+                        x[c] = acc / M[c][c]
+                    with np.errstate(over="ignore"):
+                        na = np.array(x, dtype=np.float64).astype(np.float16)
+                    if np.isfinite(na).all():
+                        a16 = na
+                vals = combos @ a16.astype(np.float64)          # value of each combination
+                best = np.argmin(np.abs(wg[:, None] - vals[None, :]), axis=1)   # first minimum
+                b = combos[best].T
+            recon = (a16.astype(np.float64)[:, None] * b).sum(axis=0)
+            err += float(((wg - recon) ** 2).sum())
+            B[:, j, t * g:(t + 1) * g] = b.astype(np.int8)
+            A[:, j, t] = a16
+    bits = np.packbits((B > 0).astype(np.uint8), axis=2, bitorder="little")
+    return bits, A, err
 
 
 def search_group_sizes(N: int, K: int, max_bits_per_weight: float, has_offset: bool = False):

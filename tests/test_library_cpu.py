@@ -312,3 +312,83 @@ def test_group_search_errors():
     assert L.bcq_search_group_sizes(4, 512, 0, 0.0, g, b) == 3
     assert L.bcq_search_group_sizes(4, 512, 0, float("nan"), g, b) == 3
     assert L.bcq_search_group_sizes(4, 512, 0, 3.0, None, b) == 1
+
+
+def _quant_input(rng, N, K, dist):
+    if dist == "gauss":
+        w = rng.standard_normal((N, K)) * 0.02
+    elif dist == "heavy":
+        w = rng.standard_t(3, (N, K)) * 0.05
+    elif dist == "large":
+        w = rng.uniform(-60000, 60000, (N, K))
+    elif dist == "tiny":
+        w = rng.standard_normal((N, K)) * 1e-6          # fp16 subnormals
+    else:
+        raise ValueError(dist)
+    w = w.astype(np.float16)
+    w[0, : K // 2] = 0                                   # a zero half-row
+    if N > 1:
+        w[1, :] = np.float16(-0.0)                       # an all (negative) zero row
+    if N > 2:
+        w[2, :] = w[2, 0]                                # a constant row
+    return w
+
+
+@pytest.mark.parametrize("N,K,q,g,iters,dist", [
+    (5, 64, 1, 8, 0, "gauss"), (4, 256, 3, 128, 0, "gauss"), (4, 256, 3, 128, 3, "gauss"),
+    (3, 96, 2, 32, 2, "heavy"), (2, 4096, 4, 4096, 1, "gauss"), (3, 64, 8, 64, 2, "gauss"),
+    (3, 128, 3, 64, 2, "large"), (3, 128, 2, 16, 2, "tiny"), (9, 40, 5, 8, 4, "heavy"),
+])
+def test_quantize_matches_oracle(N, K, q, g, iters, dist):
+    """bcq_quantize and the oracle's quantizer agree bit for bit (planes and fp16
+    scales); the squared errors agree up to summation order."""
+    rng = np.random.default_rng(N * 1000 + K + q)
+    w = _quant_input(rng, N, K, dist)
+    bits, alpha, err = lg.bcq_quantize(w, q, g, iters)
+    ob_, oa, oe = oracle.quantize_bcq(w, q, g, iters)
+    assert np.array_equal(bits, ob_)
+    assert np.array_equal(alpha.view(np.uint16), oa.view(np.uint16))
+    assert err == pytest.approx(oe, rel=1e-12, abs=1e-300)
+
+
+def test_quantize_then_pack_matches_oracle():
+    """Quantizer output feeds bcq_pack unchanged (layouts [q][N][K/8], [q][N][K/g])."""
+    rng = np.random.default_rng(7)
+    N, K, q, g = 20, 520, 3, 40
+    w = _quant_input(rng, N, K, "gauss")
+    bits, alpha, _ = lg.bcq_quantize(w, q, g, 2)
+    pb, pa, po = lg.bcq_pack(bits, alpha, None, g)
+    eb, ea, eo = oracle.pack(bits, alpha, None, g)
+    assert np.array_equal(pb, eb) and np.array_equal(pa.view(np.uint16), ea.view(np.uint16))
+
+
+def test_quantize_errors():
+    L = lg.lib()
+    N, K, q, g = 4, 64, 2, 32
+    w = (np.random.default_rng(0).standard_normal((N, K)) * 0.1).astype(np.float16)
+    w16 = w.view(np.uint16)
+    bits = np.full(q * N * K // 8, 0xAB, np.uint8)
+    alpha = np.full(q * N * K // g, 0xABCD, np.uint16)
+    err = ctypes.c_double(-1.0)
+
+    def call(shape, wp=w16, it=0, nb=bits.size, na=alpha.size, b=bits, a=alpha):
+        p = lambda t: None if t is None else t.ctypes.data
+        return L.bcq_quantize(ctypes.byref(shape), p(wp), it, p(b), nb, p(a), na, ctypes.byref(err))
+
+    s = lg.Shape(N, K, q, g, 0)
+    assert call(lg.Shape(N, K, q, g, 1)) == 2                 # no offset term in BCQ output
+    assert call(lg.Shape(N, K, q, 24, 0)) == 2                # g does not divide K
+    assert call(lg.Shape(N, K, 9, g, 0)) == 2
+    assert call(s, it=-1) == 3 and call(s, it=1001) == 3
+    assert call(s, wp=None) == 1 and call(s, b=None) == 1 and call(s, a=None) == 1
+    assert call(s, nb=bits.size - 1) == 4 and call(s, na=alpha.size - 1) == 4
+    bad = w16.copy()
+    bad[3, 63] = 0x7E00                                        # NaN
+    assert call(s, wp=bad) == 3
+    bad[3, 63] = 0xFC00                                        # -inf
+    assert call(s, wp=bad) == 3
+    assert (bits == 0xAB).all() and (alpha == 0xABCD).all()   # nothing written on error
+    assert L.bcq_quantize(None, None, 0, None, 0, None, 0, None) == 1
+    assert call(lg.Shape(0, K, q, g, 0), wp=None, b=None, a=None) == 0
+    assert err.value == 0.0
+    assert call(s) == 0 and err.value > 0

@@ -376,6 +376,113 @@ def test_parity_rule():
 
 # ---------------------------------------------------------------- planted mistakes
 
+# ---------------------------------------------------------------- quantizer
+
+def _balanced_bcq(rng, N, K, q, g, scale):
+    """W = sum_i alpha_i b_i where, inside every group, each block of 2^q weights
+    holds every sign combination once (in random order) and alpha_i =
+    scale * 2^-i. Every pairwise product b_i b_k then averages to zero over the
+    group, so the greedy step sees mean |residual| = alpha_i exactly."""
+    assert g % (1 << q) == 0
+    nc = 1 << q
+    planes = np.empty((q, N, K), np.int8)
+    for j in range(N):
+        for blk in range(K // nc):
+            perm = rng.permutation(nc)
+            for t, c in enumerate(perm):
+                for i in range(q):
+                    planes[i, j, blk * nc + t] = 1 if (c >> i) & 1 else -1
+    alpha = np.array([scale * 2.0 ** -i for i in range(q)])
+    W = sum(alpha[i] * planes[i].astype(np.float64) for i in range(q))
+    assert np.array_equal(W.astype(np.float16).astype(np.float64), W)
+    return W.astype(np.float16), planes, alpha
+
+
+@pytest.mark.parametrize("q,g,iters", [(1, 8, 0), (2, 16, 0), (3, 32, 0), (3, 32, 2), (4, 64, 3)])
+def test_quantize_recovers_exact_bcq(q, g, iters):
+    """A matrix that is exactly BCQ (with distinct combination values) comes back
+    exactly: planes in order, bits LSB-first, scales [q][N][K/g], zero error."""
+    rng = np.random.default_rng(20 + q)
+    N, K = 3, 2 * g
+    W, planes, alpha = _balanced_bcq(rng, N, K, q, g, 0.75)
+    bits, a, err = ob.quantize_bcq(W, q, g, iters)
+    assert err == 0.0
+    assert np.array_equal(bits, _encode_signs(planes))
+    for i in range(q):
+        assert np.all(a[i].astype(np.float64) == alpha[i])
+
+
+def test_quantize_q1_is_the_fp16_optimum():
+    """For one plane, the result's error equals the best over every sign vector
+    and, for each, both fp16 neighbours of its least-squares scale (exhaustive
+    over 2^8 sign vectors per group)."""
+    rng = np.random.default_rng(31)
+    g = 8
+    combos = np.array([[1.0 if (c >> k) & 1 else -1.0 for k in range(g)] for c in range(1 << g)])
+    for trial in range(40):
+        w = (rng.standard_normal(g) * rng.choice([1e-3, 0.1, 3.0])).astype(np.float16)
+        if trial % 7 == 0:
+            w[rng.integers(0, g)] = 0
+        wd = w.astype(np.float64)
+        best = np.inf
+        for b in combos:
+            a_ls = float(b @ wd) / g
+            h = np.float16(a_ls)
+            for cand in (h, np.nextafter(h, np.float16(np.inf)), np.nextafter(h, np.float16(-np.inf))):
+                e = float(((wd - float(cand) * b) ** 2).sum())
+                best = min(best, e)
+        for iters in (0, 2):
+            _, _, err = ob.quantize_bcq(w[None, :], 1, g, iters)
+            assert err == pytest.approx(best, rel=1e-12, abs=1e-30)
+
+
+def test_quantize_q2_lower_bound_and_refinement():
+    """Two planes, groups of 8: no result beats the continuous optimum (found by
+    trying all 2^16 plane pairs with least-squares scales), and the alternating
+    rounds lower the total error against the greedy start."""
+    rng = np.random.default_rng(32)
+    g = 8
+    c = np.array([[1.0 if (v >> k) & 1 else -1.0 for k in range(g)] for v in range(1 << g)])
+    B0 = np.repeat(c, len(c), axis=0)
+    B1 = np.tile(c, (len(c), 1))
+    tot0 = tot3 = 0.0
+    for _ in range(12):
+        w = (rng.standard_normal(g) * 0.05).astype(np.float16)
+        wd = w.astype(np.float64)
+        # least squares per pair: [[g, d], [d, g]] a = [B0 w, B1 w]
+        d = (B0 * B1).sum(axis=1)
+        v0, v1 = B0 @ wd, B1 @ wd
+        det = g * g - d * d
+        ok = det > 0
+        a0 = np.where(ok, (g * v0 - d * v1) / np.where(ok, det, 1), v0 / g)
+        a1 = np.where(ok, (g * v1 - d * v0) / np.where(ok, det, 1), 0.0)
+        e = ((wd[None, :] - a0[:, None] * B0 - a1[:, None] * B1) ** 2).sum(axis=1)
+        floor = e.min()
+        _, _, e0 = ob.quantize_bcq(w[None, :], 2, g, 0)
+        _, _, e3 = ob.quantize_bcq(w[None, :], 2, g, 3)
+        assert e0 >= floor * (1 - 1e-9) - 1e-18
+        assert e3 >= floor * (1 - 1e-9) - 1e-18
+        tot0 += e0
+        tot3 += e3
+    assert tot3 < tot0
+
+
+def test_quantize_error_is_the_reconstruction_error():
+    """The returned error is the squared distance between W and the returned
+    planes and scales (decoded here with explicit bit arithmetic)."""
+    rng = np.random.default_rng(33)
+    N, K, q, g = 4, 64, 3, 16
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    bits, a, err = ob.quantize_bcq(w, q, g, 2)
+    rec = np.zeros((N, K))
+    for i in range(q):
+        for j in range(N):
+            for k in range(K):
+                s = 1.0 if (int(bits[i, j, k // 8]) >> (k % 8)) & 1 else -1.0
+                rec[j, k] += float(a[i, j, k // g]) * s
+    assert err == pytest.approx(float(((w.astype(np.float64) - rec) ** 2).sum()), rel=1e-12)
+
+
 def _run_pins():
     """The pins above, as a callable that raises AssertionError on any failure."""
     test_sign_order_golden()
@@ -388,6 +495,11 @@ def _run_pins():
     test_uniform_rewrite_exhaustive(4)
     test_pack_roundtrip(17, 520, 3, 8, True)
     test_pack_single_bit_positions()
+    test_quantize_recovers_exact_bcq(3, 32, 0)
+    test_quantize_recovers_exact_bcq(3, 32, 2)
+    test_quantize_q1_is_the_fp16_optimum()
+    test_quantize_q2_lower_bound_and_refinement()
+    test_quantize_error_is_the_reconstruction_error()
 
 
 def _mut_signs_msb_first(bits):
@@ -461,7 +573,38 @@ def _mut_pack_rows_chunks_swapped(bits, alpha, offset, g):
     return pb, pa, po
 
 
+_orig_quant = ob.quantize_bcq
+
+
+def _mut_quant_planes_reversed(w, q, g, iters=0):
+    bits, a, e = _orig_quant(w, q, g, iters)
+    return bits[::-1].copy(), a[::-1].copy(), e
+
+
+def _mut_quant_alpha_one_ulp(w, q, g, iters=0):
+    bits, a, e = _orig_quant(w, q, g, iters)
+    a2 = np.nextafter(a, np.float16(np.inf))
+    rec = (np.stack([ob.signs(bits[i]) for i in range(q)]).astype(np.float64)
+           * np.repeat(a2.astype(np.float64), g, axis=2)).sum(axis=0)
+    return bits, a2, float(((np.asarray(w, np.float64) - rec) ** 2).sum())
+
+
+def _mut_quant_bits_msb_first(w, q, g, iters=0):
+    bits, a, e = _orig_quant(w, q, g, iters)
+    return np.packbits(np.unpackbits(bits, axis=-1, bitorder="little"), axis=-1, bitorder="big"), a, e
+
+
+def _mut_quant_error_first_group_only(w, q, g, iters=0):
+    bits, a, e = _orig_quant(w, q, g, iters)
+    _, _, e1 = _orig_quant(np.asarray(w)[:, :g], q, g, iters)
+    return bits, a, e1
+
+
 @pytest.mark.parametrize("name,mutant", [
+    ("quantize_bcq", _mut_quant_planes_reversed),
+    ("quantize_bcq", _mut_quant_alpha_one_ulp),
+    ("quantize_bcq", _mut_quant_bits_msb_first),
+    ("quantize_bcq", _mut_quant_error_first_group_only),
     ("signs", _mut_signs_msb_first),
     ("signs", _mut_signs_flipped),
     ("reconstruct_rows", _mut_reconstruct_drop_offset),
