@@ -32,16 +32,17 @@ __global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
 
 // ring: >= 3 asks for the deeper ring where an instance has one, 0 for the
 // default; xl: the variant with x staged in LDS (batch 1).
-KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring, bool xl) {
+KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring, bool xl,
+                     bool pr = false) {
   switch (q) {
-    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl);
-    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl);
-    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring, xl);
-    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring, xl);
-    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring, xl);
-    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring, xl);
-    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring, xl);
-    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring, xl);
+    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring, xl, pr);
     default: return nullptr;
   }
 }
@@ -51,23 +52,25 @@ struct Config {
   int RI;                // row tiles per row block (<= W * RPW)
   int ring;              // >= 3: the deeper ring; 0: the instance's default
   bool xl;               // x staged in LDS
+  bool pr;               // paired tables (two batch rows per table entry)
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
 };
 
 struct TileOverride {
-  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1;
+  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1, pr = -1;
 };
 
-// Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL]]]]]" (LUTGEMM_TILE);
+// Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR]]]]]]" (LUTGEMM_TILE);
 // never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
-// (default: where possible).
+// (default: where possible). PR: 1 paired tables where an instance has them, 0
+// never (default: the dispatcher's choice).
 bool tile_override(TileOverride* o) {
   const char* e = getenv("LUTGEMM_TILE");
   if (!e || !*e) return false;
-  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring,
-                       &o->ri, &o->xl);
+  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring,
+                       &o->ri, &o->xl, &o->pr);
   return n >= 2;
 }
 
@@ -114,12 +117,19 @@ Config choose_config(const Geometry& G, int64_t m) {
     c.S = 1;
   } else {
     double best = 1e300;
-    struct Cand { int w, rpw, mc; double eff; };
-    const Cand cands[] = {{16, 2, 1, 1.0}, {16, 1, 1, 1.0}, {8, 2, 4, 1.3}, {8, 1, 4, 1.3},
-                          {8, 2, 2, 1.3}, {8, 1, 2, 1.3}, {8, 2, 1, 1.3}, {8, 1, 1, 1.3}};
+    // eff: cost of one input tile per unit of (row tiles x batch rows) / 16;
+    // bar: cost of one input tile per batch row of the item (barriers and
+    // table builds that serialise); measured on 12288 x 12288, m = 4..32.
+    struct Cand { int w, rpw, mc; double eff, bar; bool pr; };
+    const Cand cands[] = {
+        {16, 2, 1, 1.0, 0.0, false}, {16, 1, 1, 1.0, 0.0, false}, {8, 2, 4, 0.5, 0.425, true},
+        {8, 1, 4, 0.5, 0.425, true}, {8, 2, 2, 0.5, 0.425, true}, {8, 1, 2, 0.5, 0.425, true},
+        {8, 2, 4, 0.71, 0.31, false}, {8, 1, 4, 0.71, 0.31, false}, {8, 2, 2, 0.71, 0.31, false},
+        {8, 1, 2, 0.71, 0.31, false}, {8, 2, 1, 1.3, 0.0, false},   {8, 1, 1, 1.3, 0.0, false}};
     for (const Cand& v : cands) {
       if (v.mc > 1 && m < v.mc) continue;
-      if (!pick_kernel(q, v.rpw, v.mc, c.gq, off, v.w, 0, false)) continue;
+      if (v.pr && m < 8) continue;   // measured slower than 16 waves x 1 row at m <= 4
+      if (!pick_kernel(q, v.rpw, v.mc, c.gq, off, v.w, 0, false, v.pr)) continue;
       const int64_t rows = (int64_t)v.w * v.rpw;            // row tiles per item
       const int64_t n_rb = (G.RT + rows - 1) / rows;
       const int64_t n_bg = (m + v.mc - 1) / v.mc;
@@ -129,12 +139,14 @@ Config choose_config(const Geometry& G, int64_t m) {
         const int64_t per_cu = (items + kCUs - 1) / kCUs;
         const int64_t tiles = (G.KT + s - 1) / s;
         const double unit = v.eff * (double)rows * v.mc / 16.0;
-        const double cost = (double)per_cu * (tiles * unit + 0.3 * unit) + (s > 1 ? 2.0 : 0.0);
+        const double step = unit + v.bar * v.mc;
+        const double cost = (double)per_cu * (tiles * step + 0.3 * unit) + (s > 1 ? 2.0 : 0.0);
         if (cost < best - 1e-9) {
           best = cost;
           c.W = v.w;
           c.RPW = v.rpw;
           c.MC = v.mc;
+          c.pr = v.pr;
           c.RI = (int)rows;
           c.n_rb = n_rb;
           c.n_bg = n_bg;
@@ -142,20 +154,23 @@ Config choose_config(const Geometry& G, int64_t m) {
         }
       }
     }
-    c.xl = xl_ok && pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, 0, true) != nullptr;
+    c.xl = !c.pr && xl_ok && pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, 0, true) != nullptr;
   }
   TileOverride o;
   if (tile_override(&o)) {
     const int w = o.w ? o.w : c.W;
     const int mc = o.mc ? o.mc : c.MC;
-    const bool xl = o.xl < 0 ? xl_ok && pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, true)
-                             : (o.xl > 0 && xl_ok);
-    if (pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, xl)) {
+    const bool pr = o.pr > 0;
+    const bool xl = pr ? false
+                    : o.xl < 0 ? xl_ok && pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, true)
+                               : (o.xl > 0 && xl_ok);
+    if (pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, xl, pr)) {
       c.W = w;
       c.RPW = o.rpw;
       c.MC = mc;
       c.ring = o.ring;
       c.xl = xl;
+      c.pr = pr;
       c.RI = (o.ri >= 1 && o.ri <= c.W * c.RPW) ? o.ri : c.W * c.RPW;
       c.n_rb = (G.RT + c.RI - 1) / c.RI;
       c.n_bg = (m + c.MC - 1) / c.MC;
@@ -263,7 +278,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
       return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
     }
 
-    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl);
+    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr);
     if (!fn) return LUTGEMM_ERR_INTERNAL;
     Params p{};
     p.bits = (const uint8_t*)d_bits;

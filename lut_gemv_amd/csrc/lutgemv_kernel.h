@@ -174,6 +174,7 @@ struct LaneCtx {
   uint32_t block;     // byte offset of this lane's block in a 1 KiB plane block
   uint32_t tsel[4];   // (table index 4*c4 + b_k) * 4: byte 0 of the address
   uint32_t psel[4];   // v_perm selector taking byte b_k of a sign word into byte 1
+  uint32_t ptsel[4];  // paired tables: bytes 0 and 2 of the address of chunk 4*c4 + b_k
   uint32_t aoff, ooff;  // g % 32 == 0 and g divides 512: byte offset of this lane's
                         // scales (and offsets) in a tile's scale block
 };
@@ -193,6 +194,8 @@ __device__ __forceinline__ LaneCtx lane_ctx() {
     // byte 0 <- S1 byte 0 (table index), byte 1 <- S0 byte b (sign byte),
     // byte 2 <- S1 byte 2 (table buffer), byte 3 <- 0
     l.psel[k] = 0x0C020000u | ((4u + b) << 8);
+    const uint32_t t = 4u * (uint32_t)l.c4 + b;
+    l.ptsel[k] = ((t & 31u) << 3) | ((t >> 5) << 16);
   }
   return l;
 }
@@ -343,6 +346,57 @@ __device__ __forceinline__ float lut_at(const float* lut, uint32_t byte_addr) {
   return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + byte_addr);
 }
 
+// ------------------------------------------------------------------ paired tables
+// With two or more batch rows per item the tables of two rows can share one
+// 128 KiB buffer, entry by entry: the pair (row 2h, row 2h+1) of entry p of
+// chunk t sits at byte p*256 + (t % 32)*8 + (t / 32)*64 KiB. One 64-bit read
+// then serves both rows: half the LDS instructions of two single-row lookups
+// (the LDS takes about as long per instruction for 64-bit as for 32-bit reads).
+// The bank of an entry depends only on t % 32 and each half-wave reads 32
+// different chunks, so the reads are free of bank conflicts whatever the bytes.
+// The price is one buffer instead of two: the build waits for the previous
+// lookups to finish.
+__device__ __forceinline__ float2 lut_at2(const float* lut, uint32_t byte_addr) {
+  return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(lut) + byte_addr);
+}
+
+// Paired table of lane l's chunk: the same Gray-code walk as build_table, for
+// two batch rows at once (xa: row 2h, xb: row 2h+1), one 64-bit store per entry.
+template <int W>
+__device__ __forceinline__ void build_table_pair(float* lut, const LaneCtx& l, const uint4 xa,
+                                                 const uint4 xb) {
+  constexpr int HPW = W == 16 ? 1 : 2;
+  constexpr int NB = HPW == 2 ? 5 : 4;
+  static_assert(W == 8 || W == 16, "8 or 16 waves per workgroup");
+  float x[8], y[8];
+  unpack8(xa, x);
+  unpack8(xb, y);
+  const int h0 = l.wave * HPW;
+  const float cx = ((h0 & 1) ? x[4] : -x[4]) + ((h0 & 2) ? x[5] : -x[5]);
+  const float dx = ((h0 & 4) ? x[6] : -x[6]) + ((h0 & 8) ? x[7] : -x[7]);
+  const float cy = ((h0 & 1) ? y[4] : -y[4]) + ((h0 & 2) ? y[5] : -y[5]);
+  const float dy = ((h0 & 4) ? y[6] : -y[6]) + ((h0 & 8) ? y[7] : -y[7]);
+  float T = (-(x[0] + x[1]) - (x[2] + x[3])) + (cx + dx);
+  float U = (-(y[0] + y[1]) - (y[2] + y[3])) + (cy + dy);
+  float twx[NB], twy[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    twx[t] = x[t] + x[t];
+    twy[t] = y[t] + y[t];
+  }
+  char* base = reinterpret_cast<char*>(lut) + (h0 * 16) * 256 + (l.lane & 31) * 8 +
+               (l.lane >> 5) * (kLutWords * 4);
+  *reinterpret_cast<float2*>(base) = make_float2(T, U);
+#pragma unroll
+  for (int n = 1; n < (1 << NB); ++n) {
+    const int t = __builtin_ctz(n);
+    const int pat = n ^ (n >> 1);
+    T += ((pat >> t) & 1) ? twx[t] : -twx[t];
+    U += ((pat >> t) & 1) ? twy[t] : -twy[t];
+    *reinterpret_cast<float2*>(base + pat * 256) = make_float2(T, U);
+  }
+}
+
 // Look up every row tile of batch row r in table buffer `buf`. Per plane and
 // row, a lane reads the entries its four sign bytes select; with GQ they are
 // summed and scaled once, else each is scaled by its chunk's group scale.
@@ -412,6 +466,55 @@ __device__ __forceinline__ void lookups(const LaneCtx& l, int r, int buf, const 
             const uint32_t oword = T.ow[i][2 * k + (a >> 1)];
             acc[r][i][a] = __builtin_fmaf(h2f(oword, a & 1), csum[k], acc[r][i][a]);
           }
+        }
+      }
+    }
+  }
+}
+
+// Lookups of batch rows 2h and 2h+1 from the paired table (scale groups of 32
+// or more inputs: the four chunks of a lane block share one scale).
+template <int Q, int RPW, int MC, bool OFF>
+__device__ __forceinline__ void lookups_pair(const LaneCtx& l, int h, const float* lut,
+                                             const TileRegs<Q, RPW, MC, true, OFF>& T,
+                                             float (&acc)[MC][RPW][4]) {
+  const int r0 = 2 * h, r1 = 2 * h + 1;
+  float cs0 = 0.f, cs1 = 0.f;
+  if constexpr (OFF) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 e = lut_at2(lut, (0xFFu << 8) | l.ptsel[k]);
+      cs0 = k == 0 ? e.x : cs0 + e.x;
+      cs1 = k == 0 ? e.y : cs1 + e.y;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    if (i < T.pos.c.valid_rpw) {  // uniform over the wave
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint32_t words[4] = {T.bw[i][q].x, T.bw[i][q].y, T.bw[i][q].z, T.bw[i][q].w};
+        float2 e[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            e[a][k] = lut_at2(lut, __builtin_amdgcn_perm(words[a], l.ptsel[k], l.psel[k]));
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float s0 = (e[a][0].x + e[a][1].x) + (e[a][2].x + e[a][3].x);
+          const float s1 = (e[a][0].y + e[a][1].y) + (e[a][2].y + e[a][3].y);
+          const float al = h2f(T.aw[i][q * 2 + (a >> 1)], a & 1);
+          acc[r0][i][a] = __builtin_fmaf(al, s0, acc[r0][i][a]);
+          acc[r1][i][a] = __builtin_fmaf(al, s1, acc[r1][i][a]);
+        }
+      }
+      if constexpr (OFF) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float o = h2f(T.ow[i][a >> 1], a & 1);
+          acc[r0][i][a] = __builtin_fmaf(o, cs0, acc[r0][i][a]);
+          acc[r1][i][a] = __builtin_fmaf(o, cs1, acc[r1][i][a]);
         }
       }
     }
@@ -522,13 +625,17 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // XL (batch 1 only): x is staged whole in LDS at the start, and the tables are
 // built from there, instead of every wave loading each x tile from L2 (all
 // waves of all CUs reading the same lines).
-template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL>
+// PR (two or more batch rows, grouped scales): paired tables in one buffer; each
+// tile takes, per pair of batch rows, a barrier, the pair's table build, a
+// barrier and the pair's lookups.
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL, bool PR = false>
 // The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
 // also the most that can ever run; saying so lets the scheduler use the
 // whole register budget to keep table lookups in flight.
 __global__ void __launch_bounds__(W * 64, W / 4)
     __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) lutgemv_kernel(Params p) {
   static_assert(!XL || MC == 1, "x in LDS is for batch 1");
+  static_assert(!PR || (GQ && !XL && MC % 2 == 0), "paired tables: grouped scales, even MC");
   __shared__ float lut[2 * kLutWords];
   __shared__ uint4 xs[XL ? kXChunks : 1];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
@@ -568,6 +675,34 @@ __global__ void __launch_bounds__(W * 64, W / 4)
       return T.xv[r];
     }
   };
+  if constexpr (PR) {
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        if (!done) {
+          TR& cur = R[s];
+          TR& nxt = R[(s + 1) % NR];
+          TR& pre = R[(s + NR - 1) % NR];
+          pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
+          load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, pre);
+#pragma unroll
+          for (int h = 0; h < MC / 2; ++h) {
+            if (2 * h < cur.pos.c.rows_here) {  // uniform over the workgroup
+              __syncthreads();                  // the previous lookups are done
+              build_table_pair<W>(lut, l, cur.xv[2 * h], cur.xv[2 * h + 1]);
+              __syncthreads();
+              lookups_pair<Q, RPW, MC, OFF>(l, h, lut, cur, acc);
+            }
+          }
+          if (cur.pos.kt + 1 == cur.pos.c.kt1) finish_item<RPW, MC>(p, l, cur.pos.c, acc);
+          done = !nxt.pos.live;
+        }
+      }
+    }
+    if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    return;
+  }
   int buf = 0;
   build_table<W>(lut, 0, l, xtile(R[0], 0));
   __syncthreads();
@@ -610,12 +745,13 @@ using KernelFn = void (*)(Params);
 // (four per SIMD). An instance keeps a ring of NR tiles in flight, the
 // accumulators and some temporaries in that budget: three tiles when they fit,
 // else two (16 waves use two, plus a deeper ring where it fits).
-template <int Q, int RPW, int MC, bool GQ, bool OFF, int NR, bool XL = false>
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int NR, bool XL = false, bool PR = false>
 constexpr int kVgprEstimate =
     NR * (RPW * Q * 4 + RPW * (GQ ? 2 * Q : 8 * Q) + (XL ? 0 : MC * 4) +
           (OFF ? RPW * (GQ ? 2 : 8) : 0)) +
-    4 * RPW * MC + (GQ ? 16 + 2 : 4) + 32;   // + the table entries of one lookup group in
-                                             // flight (+ lane scale offsets)
+    4 * RPW * MC + (GQ ? 16 + 2 : 4) + 32 +  // + the table entries of one lookup group in
+    (PR ? 16 + 4 : 0);                       // flight (+ lane scale offsets); paired: entry
+                                             // pairs and address selectors
 
 template <int W>
 constexpr int kBudget = W == 16 ? 128 : 256;
@@ -634,10 +770,28 @@ template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, bool XL, int NR>
 constexpr bool kFits16 =
     W == 16 && MC == 1 && GQ && kVgprEstimate<Q, RPW, MC, GQ, OFF, NR, XL> <= kBudget<W>;
 
+// Ring depth of a paired-table instance: three tiles where they fit (8 waves),
+// else two; 0 when not even two fit.
+template <int Q, int RPW, int MC, bool OFF, int W>
+constexpr int kRingPair =
+    (MC % 2 != 0) ? 0
+    : (W == 8 && kVgprEstimate<Q, RPW, MC, true, OFF, 3, false, true> + 8 <= kBudget<W>) ? 3
+    : (kVgprEstimate<Q, RPW, MC, true, OFF, 2, false, true> <= kBudget<W>) ? 2
+    : 0;
+
 // ring 3 or 4 selects a deeper ring where an instance has one (16 waves); xl
-// the x-in-LDS variant (16 waves, batch 1, grouped scales).
+// the x-in-LDS variant (16 waves, batch 1, grouped scales); pr the paired
+// tables (grouped scales, even MC).
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
-KernelFn kernel_or_null(int ring, bool xl) {
+KernelFn kernel_or_null(int ring, bool xl, bool pr) {
+  if (pr) {
+    if constexpr (GQ && kRingPair<Q, RPW, MC, OFF, W> > 0) {
+      return xl ? nullptr
+                : lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true>;
+    } else {
+      return nullptr;
+    }
+  }
   if constexpr (kInstantiated<Q, RPW, MC, GQ, OFF, W>) {
     if constexpr (W == 16 && MC == 1 && GQ) {
       if (xl) {
@@ -663,47 +817,47 @@ KernelFn kernel_or_null(int ring, bool xl) {
 }
 
 template <int Q, int RPW, int MC, int W>
-KernelFn pick_flags(bool gq, bool off, int ring, bool xl) {
+KernelFn pick_flags(bool gq, bool off, int ring, bool xl, bool pr) {
   if (gq)
-    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl)
-               : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl);
-  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring, xl)
-             : kernel_or_null<Q, RPW, MC, false, false, W>(ring, xl);
+    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl, pr)
+               : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl, pr);
+  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring, xl, pr)
+             : kernel_or_null<Q, RPW, MC, false, false, W>(ring, xl, pr);
 }
 
 template <int Q, int W>
-KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl) {
+KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool pr) {
   if (mc == 1) {
-    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl);
-    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring, xl);
+    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl, pr);
+    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring, xl, pr);
   } else if (mc == 2) {
-    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring, xl);
-    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring, xl);
+    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring, xl, pr);
+    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring, xl, pr);
   } else if (mc == 4) {
-    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring, xl);
-    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring, xl);
+    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring, xl, pr);
+    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring, xl, pr);
   }
   return nullptr;
 }
 
 // The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
 // item, scale groups aligned to 32 inputs (gq), an offset term (off), w waves
-// per workgroup, ring depth (0 default, >= 3 deeper) and x in LDS (xl), or
-// nullptr if none is built.
+// per workgroup, ring depth (0 default, >= 3 deeper), x in LDS (xl) and paired
+// tables (pr), or nullptr if none is built.
 template <int Q>
-KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl) {
-  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl);
-  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl);
+KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, bool pr) {
+  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl, pr);
+  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl, pr);
   return nullptr;
 }
 
-extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool);
-extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool);
-extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool);
-extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool);
-extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool);
-extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool);
-extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool);
-extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool);
+extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool, bool);
 
 }  // namespace lutgemm

@@ -213,6 +213,25 @@ def test_bitwise_deterministic_and_split_consistent(monkeypatch):
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# "RPW,S,W,MC,ring,RI,XL,PR": paired tables (two batch rows per table entry)
+@pytest.mark.parametrize("tile", ["1,1,8,2,0,8,0,1", "2,1,8,4,0,16,0,1", "1,3,8,4,0,5,0,1",
+                                  "2,2,8,2,0,13,0,1"])
+@pytest.mark.parametrize("N,K,q,g,m,off", [
+    (1000, 4128, 3, 32, 3, True),      # ragged rows and input tiles, odd batch
+    (300, 1536, 5, 64, 5, False),
+    (1024, 12288, 3, 128, 4, False),
+    (129, 2048, 8, 256, 7, True),
+])
+def test_paired_tables_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + q + m, with_offset=off,
+                             name=f"paired_{N}x{K}q{q}g{g}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", tile)
+    _say(f"paired tables {tile}: N={N} K={K} q={q} g={g} m={m} offset={off}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
 def test_workspace_reuse_across_shapes():
     """One workspace serves a large split call, then a smaller one, then the large again."""
     big = workloads.random_bcq(8192, 12288, 3, 128, m=1, seed=6)
