@@ -119,16 +119,21 @@ Config choose_config(const Geometry& G, int64_t m) {
     double best = 1e300;
     // eff: cost of one input tile per unit of (row tiles x batch rows) / 16;
     // bar: cost of one input tile per batch row of the item (barriers and
-    // table builds that serialise); measured on 12288 x 12288, m = 4..32.
-    struct Cand { int w, rpw, mc; double eff, bar; bool pr; };
+    // table builds that serialise); min_m: smallest batch the candidate is
+    // considered for. Measured on 12288 x 12288, m = 4..32: paired tables lost
+    // to 16 waves x 1 row at m = 4, and 16-wave paired instances to 8-wave ones
+    // at m = 8 (they win from m = 12 on).
+    struct Cand { int w, rpw, mc; double eff, bar; bool pr; int min_m; };
     const Cand cands[] = {
-        {16, 2, 1, 1.0, 0.0, false}, {16, 1, 1, 1.0, 0.0, false}, {8, 2, 4, 0.5, 0.425, true},
-        {8, 1, 4, 0.5, 0.425, true}, {8, 2, 2, 0.5, 0.425, true}, {8, 1, 2, 0.5, 0.425, true},
-        {8, 2, 4, 0.71, 0.31, false}, {8, 1, 4, 0.71, 0.31, false}, {8, 2, 2, 0.71, 0.31, false},
-        {8, 1, 2, 0.71, 0.31, false}, {8, 2, 1, 1.3, 0.0, false},   {8, 1, 1, 1.3, 0.0, false}};
+        {16, 2, 1, 1.0, 0.0, false, 1},    {16, 1, 1, 1.0, 0.0, false, 1},
+        {16, 1, 2, 0.5, 0.28, true, 12},   {8, 2, 4, 0.5, 0.425, true, 8},
+        {8, 1, 4, 0.5, 0.425, true, 8},    {8, 2, 2, 0.5, 0.425, true, 8},
+        {8, 1, 2, 0.5, 0.425, true, 8},    {8, 2, 4, 0.71, 0.31, false, 4},
+        {8, 1, 4, 0.71, 0.31, false, 4},   {8, 2, 2, 0.71, 0.31, false, 2},
+        {8, 1, 2, 0.71, 0.31, false, 2},   {8, 2, 1, 1.3, 0.0, false, 1},
+        {8, 1, 1, 1.3, 0.0, false, 1}};
     for (const Cand& v : cands) {
-      if (v.mc > 1 && m < v.mc) continue;
-      if (v.pr && m < 8) continue;   // measured slower than 16 waves x 1 row at m <= 4
+      if (m < v.min_m) continue;
       if (!pick_kernel(q, v.rpw, v.mc, c.gq, off, v.w, 0, false, v.pr)) continue;
       const int64_t rows = (int64_t)v.w * v.rpw;            // row tiles per item
       const int64_t n_rb = (G.RT + rows - 1) / rows;
@@ -140,7 +145,10 @@ Config choose_config(const Geometry& G, int64_t m) {
         const int64_t tiles = (G.KT + s - 1) / s;
         const double unit = v.eff * (double)rows * v.mc / 16.0;
         const double step = unit + v.bar * v.mc;
-        const double cost = (double)per_cu * (tiles * step + 0.3 * unit) + (s > 1 ? 2.0 : 0.0);
+        // per item: filling and draining the pipeline, about one tile step for
+        // several batch rows (measured: short batched items lose to long ones)
+        const double fix = v.mc > 1 ? step : 0.3 * unit;
+        const double cost = (double)per_cu * (tiles * step + fix) + (s > 1 ? 2.0 : 0.0);
         if (cost < best - 1e-9) {
           best = cost;
           c.W = v.w;

@@ -771,12 +771,15 @@ constexpr bool kFits16 =
     W == 16 && MC == 1 && GQ && kVgprEstimate<Q, RPW, MC, GQ, OFF, NR, XL> <= kBudget<W>;
 
 // Ring depth of a paired-table instance: three tiles where they fit (8 waves),
-// else two; 0 when not even two fit.
+// else two; 0 when not even two fit. At 16 waves the estimate is allowed 8
+// registers over the budget: it counts every entry pair of a lookup group as
+// live at once, and the compiler fits those instances (q <= 3, one row tile,
+// two batch rows) in 105-113 registers without spilling.
 template <int Q, int RPW, int MC, bool OFF, int W>
 constexpr int kRingPair =
     (MC % 2 != 0) ? 0
     : (W == 8 && kVgprEstimate<Q, RPW, MC, true, OFF, 3, false, true> + 8 <= kBudget<W>) ? 3
-    : (kVgprEstimate<Q, RPW, MC, true, OFF, 2, false, true> <= kBudget<W>) ? 2
+    : (kVgprEstimate<Q, RPW, MC, true, OFF, 2, false, true> <= kBudget<W> + (W == 16 ? 8 : 0)) ? 2
     : 0;
 
 // ring 3 or 4 selects a deeper ring where an instance has one (16 waves); xl

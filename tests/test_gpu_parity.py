@@ -215,7 +215,7 @@ def test_bitwise_deterministic_and_split_consistent(monkeypatch):
 
 # "RPW,S,W,MC,ring,RI,XL,PR": paired tables (two batch rows per table entry)
 @pytest.mark.parametrize("tile", ["1,1,8,2,0,8,0,1", "2,1,8,4,0,16,0,1", "1,3,8,4,0,5,0,1",
-                                  "2,2,8,2,0,13,0,1"])
+                                  "2,2,8,2,0,13,0,1", "1,2,16,2,0,16,0,1", "1,1,16,2,0,11,0,1"])
 @pytest.mark.parametrize("N,K,q,g,m,off", [
     (1000, 4128, 3, 32, 3, True),      # ragged rows and input tiles, odd batch
     (300, 1536, 5, 64, 5, False),
