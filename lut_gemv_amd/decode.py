@@ -18,8 +18,8 @@ What is modelled and what is not:
   * attention over the key/value cache, normalisations, activation functions
     and residual additions are not part of the kernel and are left out: the
     output projection reads the first d entries of the fused QKV output in
-    place of the attention output, and the down projection reads the up
-    projection's output in place of the gated activation;
+    place of the attention output, and the down projection reads the up half
+    of the fused gate/up output in place of the gated activation;
   * scales are drawn so that one product keeps the activations' root mean
     square roughly unchanged (|N(0, sigma)| with sigma = 1/sqrt(q K)), so a
     deep chain stays finite in fp16.
@@ -47,12 +47,14 @@ __all__ = ["MODELS", "Projection", "DecodeStack", "weight_bytes_per_token", "mai
 @dataclass(frozen=True)
 class Projection:
     """One linear layer of a decoder layer: y [N] = W [N][K] x, x read from `src`
-    (the layer input "x" or an earlier projection's output, first K entries)."""
+    (the layer input "x" or an earlier projection's output), entries
+    src_off .. src_off + K - 1."""
 
     name: str
     N: int
     K: int
     src: str
+    src_off: int = 0
 
 
 def _opt(d: int) -> List[Projection]:
@@ -61,9 +63,10 @@ def _opt(d: int) -> List[Projection]:
 
 
 def _llama(d: int, f: int) -> List[Projection]:
+    # gate and up read the same input, so they are one product of 2f rows (as
+    # inference engines fuse them); down reads the up half
     return [Projection("qkv", 3 * d, d, "x"), Projection("out", d, d, "qkv"),
-            Projection("gate", f, d, "out"), Projection("up", f, d, "out"),
-            Projection("down", d, f, "up")]
+            Projection("gate_up", 2 * f, d, "out"), Projection("down", d, f, "gate_up", f)]
 
 
 # name -> (decoder layers, projections of one layer, index of the layer output)
@@ -142,9 +145,9 @@ class DecodeStack:
         return weight_bytes_per_token(self.model, self.q, self.g, self.layers)
 
     # ------------------------------------------------------------ one token
-    def _src(self, name: str, K: int, x_layer):
-        t = x_layer if name == "x" else self.outs[name]
-        return t[:, :K] if t.shape[1] != K else t
+    def _src(self, p: Projection, x_layer):
+        t = x_layer if p.src == "x" else self.outs[p.src]
+        return t[:, p.src_off:p.src_off + p.K] if t.shape[1] != p.K else t
 
     def token(self, kernel: str = "lut"):
         """Run every product of every layer once, in order, on the current stream.
@@ -153,7 +156,7 @@ class DecodeStack:
         x_layer = self.x
         for l, lw in enumerate(self.weights):
             for p in self.projs:
-                src = self._src(p.src, p.K, x_layer)
+                src = self._src(p, x_layer)
                 if src.shape[1] != p.K or not src.is_contiguous():
                     src = src.contiguous()
                 w = lw[p.name]
@@ -211,7 +214,7 @@ class DecodeStack:
         p = next(pp for pp in self.projs if pp.name == name)
         self.token(kernel)                       # fills every source buffer
         torch.cuda.synchronize()
-        src = self._src(p.src, p.K, self.outs[self.out_name]).contiguous()
+        src = self._src(p, self.outs[self.out_name]).contiguous()
 
         def run():
             for lw in self.weights:

@@ -15,6 +15,8 @@ def test_weight_bytes_closed_form():
     d, f = 8192, 22016
     assert decode.weight_bytes_per_token("llama65b", 3, 128) == \
         int(80 * (4 * d * d + 3 * d * f) * per_weight)
+    d, f = 4096, 11008                                  # 11008 rows pad to 16, inputs to 512
+    assert decode.weight_bytes_per_token("llama7b", 3, 128) > int(32 * (4 * d * d + 3 * d * f) * per_weight)
 
 
 def test_projection_chain_is_well_formed():
@@ -22,7 +24,7 @@ def test_projection_chain_is_well_formed():
         sizes = {"x": projs[0].K}
         for p in projs:
             assert p.src in sizes, (name, p)
-            assert sizes[p.src] >= p.K, (name, p)      # reads the first K entries
+            assert sizes[p.src] >= p.src_off + p.K, (name, p)   # reads K entries from src_off
             sizes[p.name] = p.N
         assert sizes[out] == projs[0].K                 # layer output feeds the next layer
 
@@ -30,6 +32,7 @@ def test_projection_chain_is_well_formed():
 def test_stack_layers_hold_their_own_copies():
     st = decode.DecodeStack("llama7b", layers=2, device="cpu")
     assert st.bytes_per_token() == decode.weight_bytes_per_token("llama7b", 3, 128, 2)
+    assert [p.name for p in st.projs] == ["qkv", "out", "gate_up", "down"]
     a, b = st.weights[0]["down"], st.weights[1]["down"]
     assert a.d_bits.data_ptr() != b.d_bits.data_ptr()
     assert torch.equal(a.d_bits, b.d_bits) and torch.equal(a.d_alpha, b.d_alpha)

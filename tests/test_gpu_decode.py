@@ -40,7 +40,8 @@ def test_every_product_matches_oracle(stack):
     x_layer = stack.x
     for l, lw in enumerate(stack.weights):
         for p in stack.projs:
-            src = (x_layer if p.src == "x" else stack.outs[p.src])[:, :p.K].contiguous()
+            src = (x_layer if p.src == "x" else stack.outs[p.src])[:, p.src_off:p.src_off + p.K]
+            src = src.contiguous()
             y = lw[p.name](src)
             torch.cuda.synchronize()
             w = stack.logical[(p.N, p.K)]
