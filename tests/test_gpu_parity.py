@@ -254,3 +254,20 @@ def test_large_batch_and_many_rows():
     _say("N=200000")
     pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
     _check(_gpu_y(pw, w.x), w, rows=_sample_rows(w.N, 2048))
+
+
+def test_quantized_fp16_matrix_end_to_end():
+    """fp16 W -> bcq_quantize -> bcq_pack -> lutgemm_run, against the oracle's
+    product of the oracle's own quantization of the same W (bit-identical)."""
+    rng = np.random.default_rng(12)
+    N, K, q, g, m = 700, 2048, 3, 64, 3
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((m, K)).astype(np.float16)
+    bits, alpha, _ = lg.bcq_quantize(W, q, g, iters=2)
+    ob, oa, _ = oracle.quantize_bcq(W[:64], q, g, 2)            # a slice, for time
+    assert np.array_equal(bits[:, :64], ob) and np.array_equal(alpha[:, :64].view(np.uint16),
+                                                               oa.view(np.uint16))
+    _say("quantize -> pack -> run")
+    pw = lg.PackedBCQ.from_bcq(bits, alpha, None, g)
+    w = workloads.Workload("quantized", N, K, q, g, m, x, bits, alpha, None)
+    _check(_gpu_y(pw, x), w)
