@@ -392,3 +392,54 @@ def test_quantize_errors():
     assert call(lg.Shape(0, K, q, g, 0), wp=None, b=None, a=None) == 0
     assert err.value == 0.0
     assert call(s) == 0 and err.value > 0
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/lutgemm.h compiles as strict C99 and a C program links against the
+    library and calls its host entry points (no torch, no Python)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "lutgemm.h"
+int main(void) {
+  lutgemm_shape s;
+  size_t nb = 0, na = 0, no = 0;
+  uint8_t bits[2 * 16 * 512 / 8];
+  uint16_t alpha[2 * 16 * 4];
+  static uint8_t pb[2 * 1024];
+  static uint16_t pa[2 * 16 * 4];
+  uint64_t fb = 0;
+  int32_t gs[8];
+  uint64_t bs[8];
+  memset(&s, 0, sizeof s);
+  s.N = 16; s.K = 512; s.q = 2; s.g = 128; s.has_offset = 0;
+  if (lutgemm_abi_version() != LUTGEMM_ABI_VERSION) return 1;
+  if (lutgemm_check_shape(&s) != LUTGEMM_OK) return 2;
+  if (lutgemm_packed_sizes(&s, &nb, &na, &no) != LUTGEMM_OK) return 3;
+  if (nb != sizeof pb || na != sizeof pa / sizeof pa[0] || no != 0) return 4;
+  memset(bits, 0xA5, sizeof bits);
+  for (size_t i = 0; i < sizeof alpha / sizeof alpha[0]; ++i) alpha[i] = 0x3C00; /* 1.0 */
+  if (bcq_pack(&s, bits, alpha, NULL, pb, nb, pa, na, NULL, 0) != LUTGEMM_OK) return 5;
+  if (bcq_footprint_bits(&s, &fb) != LUTGEMM_OK || fb != 2u * 16 * 512 + 16u * 2 * 16 * 4) return 6;
+  if (bcq_search_group_sizes(16, 512, 0, 3.0, gs, bs) != LUTGEMM_OK) return 7;
+  if (lutgemm_run(NULL, 1, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) != LUTGEMM_ERR_NULL) return 8;
+  printf("%s\n", lutgemm_status_string(LUTGEMM_ERR_SHAPE));
+  return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(lg.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        f"-I{os.path.join(ROOT, 'include')}", str(src), f"-L{libdir}",
+                        "-l:" + os.path.basename(lg.LIB_PATH), f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.strip() == lg.status_string(2)
