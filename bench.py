@@ -54,14 +54,15 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch from rocprofv3 counters, if taken on this kernel source."""
+def stored_traffic(workload):
+    """HBM bytes per launch from rocprofv3 counters, if taken on this kernel source
+    and this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash():
+    if t.get("kernel_sha256_16") != kernel_hash() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -207,7 +208,8 @@ def main():
     ms_per_step = t_total * 1e3 / K_steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / avg_kernel_s / 1e9
-    traffic = stored_traffic() if args.kernel == "lut" else None
+    # counters were taken with the default rotation (weights streamed from HBM)
+    traffic = stored_traffic(w.name) if args.kernel == "lut" and args.rotate == 0 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -231,6 +233,7 @@ def main():
         "us_per_gemv": round(ms_per_step * 1e3, 2),
         "us_per_gemv_gpu_clock": round(avg_kernel_s * 1e6, 2),
         "us_per_gemv_single_launch_median": round(float(np.median(durs_ms)) * 1e3, 2),
+        "lookups_per_s": round(w.m * w.N * w.q * (w.K // 8) / avg_kernel_s, 0),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

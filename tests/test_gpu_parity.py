@@ -79,6 +79,33 @@ def test_opt175b_ffn_up_sampled():
     _check(y, w, rows=_sample_rows(w.N, 2048))
 
 
+def test_opt175b_ffn_up_shard_all_outputs():
+    """One of eight row shards of the FFN-up matrix, every output."""
+    w = workloads.generate("opt175b_ffn_up_shard8")
+    _say("opt175b_ffn_up_shard8 6144x12288 q3 g128 m1")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    _check(_gpu_y(pw, w.x), w)
+
+
+def test_linearity():
+    """y(x1 + x2) = y(x1) + y(x2) within the tolerance of the two sides (x1, x2
+    and their sum exact in fp16: multiples of 1/4 below 64)."""
+    rng = np.random.default_rng(21)
+    w = workloads.random_bcq(3000, 4096, 3, 128, m=1, seed=21, with_offset=True)
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    x1 = (rng.integers(-64, 64, size=(1, w.K)) / 4).astype(np.float16)
+    x2 = (rng.integers(-64, 64, size=(1, w.K)) / 4).astype(np.float16)
+    xs = (x1.astype(np.float64) + x2.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(xs.astype(np.float64), x1.astype(np.float64) + x2.astype(np.float64))
+    _say("linearity")
+    y1, y2, ys = (_gpu_y(pw, v).astype(np.float64) for v in (x1, x2, xs))
+    _, b1 = oracle.gemv(w.bits, w.alpha, w.offset, x1, w.g)
+    _, b2 = oracle.gemv(w.bits, w.alpha, w.offset, x2, w.g)
+    _, bs = oracle.gemv(w.bits, w.alpha, w.offset, xs, w.g)
+    lim = 1e-3 * (b1 + b2 + bs) + 3e-4
+    assert np.all(np.abs(ys - (y1 + y2)) <= lim)
+
+
 def test_llama7b_int4_uniform_all_outputs():
     w = workloads.generate("llama7b_mlp_int4")
     _say("llama7b_mlp_int4 11008x4096 int4 zero 8 -> BCQ q4 + offset")

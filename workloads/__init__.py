@@ -137,6 +137,11 @@ def _opt175b_ffn_up():
     return random_bcq(49152, 12288, 3, 128, 1, seed=1, name="opt175b_ffn_up")
 
 
+def _opt175b_ffn_up_shard8():
+    # one GPU's rows of the FFN-up matrix split by rows over eight GPUs
+    return random_bcq(6144, 12288, 3, 128, 1, seed=5, name="opt175b_ffn_up_shard8")
+
+
 def _llama7b_mlp_int4():
     return random_uniform(11008, 4096, 4, 128, 1, seed=2, zero=8,
                           name="llama7b_mlp_int4")
@@ -178,6 +183,9 @@ WORKLOADS = {
     "tiny": (_tiny, "x[1x512] N(0,1); W 512x512 BCQ q=3 g=128; seed 0"),
     "opt175b_ffn_up": (_opt175b_ffn_up,
                        "x[1x12288] N(0,1); W 49152x12288 BCQ q=3 g=128; seed 1"),
+    "opt175b_ffn_up_shard8": (_opt175b_ffn_up_shard8,
+                              "x[1x12288] N(0,1); W 6144x12288 BCQ q=3 g=128 (one of eight "
+                              "row shards of the FFN-up matrix); seed 5"),
     "llama7b_mlp_int4": (_llama7b_mlp_int4,
                          "x[1x4096]; W 11008x4096 uniform int4, zero 8, g=128 "
                          "-> BCQ q=4 + offset; seed 2"),
