@@ -651,6 +651,17 @@ __global__ void __launch_bounds__(W * 64, W / 4)
 #pragma unroll
       for (int a = 0; a < 4; ++a) acc[r][i][a] = 0.f;
 
+  // XL: the loads of x are issued first, all at once (NX per thread, reads past
+  // the end of x return zero), then those of the first tiles; the stores into
+  // LDS wait only for x. The first table build waits for these loads, so their
+  // latency is paid once, not once per loop trip.
+  constexpr int NX = XL ? (kXChunks + W * 64 - 1) / (W * 64) : 1;
+  uint4 xr[NX];
+  if constexpr (XL) {
+    const auto xrs = make_rsrc(p.x, (uint32_t)p.K * 2u);
+#pragma unroll
+    for (int j = 0; j < NX; ++j) xr[j] = load16(xrs, ((uint32_t)threadIdx.x + (uint32_t)(j * W * 64)) * 16u);
+  }
   TR R[NR];
   R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
   if (!R[0].pos.live) return;
@@ -660,11 +671,13 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
     load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[s]);
   }
-  if constexpr (XL) {   // chunk c of x at xs[c]; zero past the end of x
-    const uint4* xg = reinterpret_cast<const uint4*>(p.x);
-    const int C = p.K / 8;
-    for (int c = (int)threadIdx.x; c < p.KT * kChunkTile; c += W * 64)
-      xs[c] = c < C ? xg[c] : uint4{0u, 0u, 0u, 0u};
+  if constexpr (XL) {   // chunk c of x at xs[c], for the KT input tiles (zero past K)
+    const int nchunks = p.KT * kChunkTile;
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const int c = (int)threadIdx.x + j * W * 64;
+      if (c < nchunks) xs[c] = xr[j];
+    }
     __syncthreads();
   }
   // activations of chunk `lane` of a tile, for the table build
