@@ -605,10 +605,23 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
       const int row = rb * kRows + (rem - r * kRows);
       const int rr = bg * MC + r;
       if (row >= p.N || rr >= p.m) continue;
+      // the partials are read eight at a time, all eight in flight together
+      // (one memory round trip per eight splits), and added in split order
+      const float* part = p.partial + (size_t)rr * p.Npad + row;
+      const size_t sstride = (size_t)p.m * p.Npad;
       float sum = 0.f;
-      for (int s = 0; s < p.S; ++s)
-        sum += __hip_atomic_load(&p.partial[((size_t)s * p.m + rr) * p.Npad + row],
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int s0 = 0; s0 < p.S; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int s = min(s0 + u, p.S - 1);   // past the last split: a valid slot, unused
+          v[u] = __hip_atomic_load(part + (size_t)s * sstride, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < p.S) sum += v[u];
+      }
       p.y[(size_t)rr * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)sum);
     }
     __syncthreads();
