@@ -146,10 +146,14 @@ int bcq_pack_uniform(const lutgemm_shape* s, const uint8_t* codes,
  * Alignment (else LUTGEMM_ERR_ALIGN): d_bits, d_x and d_workspace 16 bytes,
  * d_alpha and d_offset 4 bytes, d_y 2 bytes.
  * Arithmetic: table entries, scaling and accumulation in fp32; y rounded to
- * fp16 to nearest-even. Results are bitwise reproducible for a fixed shape and
- * batch. All argument checks run before any HIP call; on error nothing is
- * launched. Faults inside the kernel surface at the caller's next
- * synchronization of `stream`. */
+ * fp16 to nearest-even. The launch configuration (waves, rows per item, batch
+ * rows per item, split of the input dimension) is chosen from the shape and m;
+ * results are bitwise reproducible for a fixed shape and batch. (The
+ * environment variable LUTGEMM_TILE, a tuning aid, overrides that choice; the
+ * results then stay within the same tolerance but may round differently.)
+ * All argument checks run before any HIP call; on error nothing is launched.
+ * Faults inside the kernel surface at the caller's next synchronization of
+ * `stream`. */
 int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits,
                 const void* d_alpha, const void* d_offset, const void* d_x,
                 void* d_y, void* d_workspace, size_t workspace_bytes,
