@@ -41,7 +41,7 @@ import numpy as np
 
 from . import PackedBCQ, packed_sizes
 
-__all__ = ["MODELS", "Projection", "DecodeStack", "weight_bytes_per_token", "main"]
+__all__ = ["MODELS", "Projection", "DecodeStack", "weight_bytes_per_step", "main"]
 
 
 @dataclass(frozen=True)
@@ -77,10 +77,10 @@ MODELS: Dict[str, Tuple[int, List[Projection], str]] = {
 }
 
 
-def weight_bytes_per_token(model: str, q: int = 3, g: int = 128,
+def weight_bytes_per_step(model: str, q: int = 3, g: int = 128,
                            layers: Optional[int] = None) -> int:
     """Packed bytes (sign planes + fp16 scales) of every projection of every layer:
-    what one decode step at batch 1 reads from memory, at the least."""
+    what one decode step reads from memory, at the least (whatever the batch)."""
     full_layers, projs, _ = MODELS[model]
     tot = 0
     for p in projs:
@@ -140,9 +140,9 @@ class DecodeStack:
         self.graph_kernel = None
 
     # ------------------------------------------------------------ sizes
-    def bytes_per_token(self) -> int:
-        """Packed weight bytes every token reads (bits + scales, all layers)."""
-        return weight_bytes_per_token(self.model, self.q, self.g, self.layers)
+    def bytes_per_step(self) -> int:
+        """Packed weight bytes every decode step reads (bits + scales, all layers)."""
+        return weight_bytes_per_step(self.model, self.q, self.g, self.layers)
 
     # ------------------------------------------------------------ one token
     def _src(self, p: Projection, x_layer):
@@ -185,7 +185,8 @@ class DecodeStack:
         return g
 
     def time_tokens(self, kernel: str = "lut", tokens: int = 20, warmup: int = 5) -> dict:
-        """ms per token, replaying the captured token graph."""
+        """Time of one decode step (one token for each of the m sequences),
+        replaying the captured step graph `tokens` times."""
         import torch
         if self.graph is None or self.graph_kernel != kernel:
             self.capture(kernel)
@@ -201,8 +202,9 @@ class DecodeStack:
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / tokens
         ms = e0.elapsed_time(e1) / tokens
-        return {"kernel": kernel, "ms_per_token": ms, "wall_ms_per_token": wall,
-                "GBps": self.bytes_per_token() / (ms * 1e-3) / 1e9}
+        return {"kernel": kernel, "ms_per_step": ms, "wall_ms_per_step": wall,
+                "tokens_per_s": self.m / (ms * 1e-3),
+                "GBps": self.bytes_per_step() / (ms * 1e-3) / 1e9}
 
 
     def time_projection(self, name: str, kernel: str = "lut", reps: int = 10,
@@ -250,7 +252,8 @@ def main(argv=None) -> int:
     ap.add_argument("--layers", type=int, default=None, help="decoder layers (default: the model's)")
     ap.add_argument("--q", type=int, default=3)
     ap.add_argument("--g", type=int, default=128)
-    ap.add_argument("--m", type=int, default=1, help="batch rows per token step")
+    ap.add_argument("--m", type=int, default=1,
+                    help="sequences decoded together (batch rows of every product)")
     ap.add_argument("--tokens", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--kernel", default="both", choices=["lut", "dequant", "both"])
@@ -267,7 +270,7 @@ def main(argv=None) -> int:
                      log=lambda msg: print(f"[decode] {msg}", flush=True))
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
-    print(f"[decode] {a.model}: {st.layers} layers, {st.bytes_per_token() / 1e9:.2f} GB packed "
+    print(f"[decode] {a.model}: {st.layers} layers, {st.bytes_per_step() / 1e9:.2f} GB packed "
           f"weights, set up in {setup_s:.1f} s", flush=True)
     res = {}
     kernels = ["lut", "dequant"] if a.kernel == "both" else [a.kernel]
@@ -276,7 +279,8 @@ def main(argv=None) -> int:
         y = st.outs[st.out_name]
         r["finite"] = bool(torch.isfinite(y).all().item())
         res[k] = r
-        print(f"[decode] {k}: {r['ms_per_token']:.3f} ms/token ({r['GBps']:.0f} GB/s)", flush=True)
+        print(f"[decode] {k}: {r['ms_per_step']:.3f} ms per step of {st.m} token(s) "
+              f"({r['tokens_per_s']:.0f} tokens/s, {r['GBps']:.0f} GB/s of weights)", flush=True)
     if a.breakdown:
         for k in kernels:
             rows = []
@@ -287,10 +291,10 @@ def main(argv=None) -> int:
                       f"({r['GBps']:.0f} GB/s)", flush=True)
             res[k]["breakdown"] = rows
     line = {"model": a.model, "layers": st.layers, "q": a.q, "g": a.g, "m": a.m,
-            "weight_bytes_per_token": st.bytes_per_token(), "gemvs_per_token":
+            "weight_bytes_per_step": st.bytes_per_step(), "gemvs_per_step":
             st.layers * len(st.projs), "tokens": a.tokens, "results": res}
     if "lut" in res and "dequant" in res:
-        line["dequant_over_lut"] = res["dequant"]["ms_per_token"] / res["lut"]["ms_per_token"]
+        line["dequant_over_lut"] = res["dequant"]["ms_per_step"] / res["lut"]["ms_per_step"]
     print(json.dumps(line), flush=True)
     return 0
 

@@ -11,12 +11,12 @@ def test_weight_bytes_closed_form():
     bytes of scales per weight."""
     d = 12288
     per_weight = 3 / 8 + 2 * 3 / 128
-    assert decode.weight_bytes_per_token("opt175b", 3, 128) == int(96 * 12 * d * d * per_weight)
+    assert decode.weight_bytes_per_step("opt175b", 3, 128) == int(96 * 12 * d * d * per_weight)
     d, f = 8192, 22016
-    assert decode.weight_bytes_per_token("llama65b", 3, 128) == \
+    assert decode.weight_bytes_per_step("llama65b", 3, 128) == \
         int(80 * (4 * d * d + 3 * d * f) * per_weight)
     d, f = 4096, 11008                                  # 11008 rows pad to 16, inputs to 512
-    assert decode.weight_bytes_per_token("llama7b", 3, 128) > int(32 * (4 * d * d + 3 * d * f) * per_weight)
+    assert decode.weight_bytes_per_step("llama7b", 3, 128) > int(32 * (4 * d * d + 3 * d * f) * per_weight)
 
 
 def test_projection_chain_is_well_formed():
@@ -31,13 +31,13 @@ def test_projection_chain_is_well_formed():
 
 def test_stack_layers_hold_their_own_copies():
     st = decode.DecodeStack("llama7b", layers=2, device="cpu")
-    assert st.bytes_per_token() == decode.weight_bytes_per_token("llama7b", 3, 128, 2)
+    assert st.bytes_per_step() == decode.weight_bytes_per_step("llama7b", 3, 128, 2)
     assert [p.name for p in st.projs] == ["qkv", "out", "gate_up", "down"]
     a, b = st.weights[0]["down"], st.weights[1]["down"]
     assert a.d_bits.data_ptr() != b.d_bits.data_ptr()
     assert torch.equal(a.d_bits, b.d_bits) and torch.equal(a.d_alpha, b.d_alpha)
     nbytes = sum(w.d_bits.numel() + 2 * w.d_alpha.numel() for lw in st.weights for w in lw.values())
-    assert nbytes == st.bytes_per_token()
+    assert nbytes == st.bytes_per_step()
     # scales keep one product's gain near one: sigma = 1/sqrt(q K)
     al = a.d_alpha.view(torch.float16).float().numpy()
     rms = float(np.sqrt((al[al != 0] ** 2).mean()))
