@@ -53,9 +53,11 @@ __device__ __forceinline__ int dq_group(const DqParams& p, int k) {
   return p.g_shift >= 0 ? (k >> p.g_shift) : (k / p.g);
 }
 
-// Q planes; OFF: offset term; MB: batch rows per launch (1 or 8). Each chunk
-// finds its own scale group, so any group size works.
-template <int Q, bool OFF, int MB>
+// Q planes; OFF: offset term; MB: batch rows per launch (1 or 8); GQ: the 32
+// inputs of a lane's block share one scale group (g % 32 == 0), so the lane's
+// scales are loaded and broadcast once per input tile; otherwise each chunk
+// finds its own group, so any group size works.
+template <int Q, bool OFF, int MB, bool GQ>
 __global__ void __launch_bounds__(kDqWaves * 64) dequant_gemv_kernel(DqParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -89,11 +91,29 @@ __global__ void __launch_bounds__(kDqWaves * 64) dequant_gemv_kernel(DqParams p)
         xv[r][b] = in ? *reinterpret_cast<const uint4*>(p.x + (size_t)(r0 + r) * p.K + k0 + 8 * b)
                       : uint4{0u, 0u, 0u, 0u};
       }
+    // GQ: the (alpha, alpha) pairs of the lane's four rows, per plane, for the
+    // group of its 32 inputs (and the offsets), loaded once per input tile
+    uint32_t alq[GQ ? Q : 1][4], ofq[4];
+    if constexpr (GQ) {
+      const int grp = k0 < p.K ? dq_group(p, k0) : 0;
+      const uint32_t* ab = p.alpha + ((size_t)rt * p.G + grp) * (8 * Q) + 2 * r4;
+#pragma unroll
+      for (int i = 0; i < Q; ++i) {
+        const uint2 v = *reinterpret_cast<const uint2*>(ab + i * 8);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) alq[i][a] = bcast_half(a < 2 ? v.x : v.y, a & 1);
+      }
+      if constexpr (OFF) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p.offset + ((size_t)rt * p.G + grp) * 8 + 2 * r4);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) ofq[a] = bcast_half(a < 2 ? v.x : v.y, a & 1);
+      }
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int kc = k0 + 8 * b;
       if (kc >= p.K) continue;                  // padded chunk: nothing to add
-      const int grp = dq_group(p, kc);
+      const int grp = GQ ? 0 : dq_group(p, kc);
       const uint32_t* ab = p.alpha + ((size_t)rt * p.G + grp) * (8 * Q);   // [plane][16 rows]
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -106,7 +126,7 @@ __global__ void __launch_bounds__(kDqWaves * 64) dequant_gemv_kernel(DqParams p)
           // lands on bit 15 and bit 2u+1 on bit 31 after a left shift by 15-2u
           const uint32_t nb = __builtin_amdgcn_ubfe(~words[a], 8 * b, 8);
           const uint32_t xs = nb | (nb << 15);
-          const uint32_t al = bcast_half(ab[i * 8 + (row >> 1)], row & 1);
+          const uint32_t al = GQ ? alq[i][a] : bcast_half(ab[i * 8 + (row >> 1)], row & 1);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             // (alpha, alpha) with each half negated where its sign bit is 0
@@ -117,7 +137,7 @@ __global__ void __launch_bounds__(kDqWaves * 64) dequant_gemv_kernel(DqParams p)
         }
         if constexpr (OFF) {
           const uint32_t* ob = p.offset + ((size_t)rt * p.G + grp) * 8;
-          const h2 o = __builtin_bit_cast(h2, bcast_half(ob[row >> 1], row & 1));
+          const h2 o = __builtin_bit_cast(h2, GQ ? ofq[a] : bcast_half(ob[row >> 1], row & 1));
 #pragma unroll
           for (int u = 0; u < 4; ++u) w[u] = w[u] + o;
         }
@@ -150,22 +170,29 @@ __global__ void __launch_bounds__(kDqWaves * 64) dequant_gemv_kernel(DqParams p)
 
 using DqFn = void (*)(DqParams);
 
-template <int Q>
+template <int Q, bool GQ>
 DqFn dq_pick(bool off, int mb) {
-  if (mb == 1) return off ? dequant_gemv_kernel<Q, true, 1> : dequant_gemv_kernel<Q, false, 1>;
-  return off ? dequant_gemv_kernel<Q, true, kDqMaxBatch> : dequant_gemv_kernel<Q, false, kDqMaxBatch>;
+  if (mb == 1)
+    return off ? dequant_gemv_kernel<Q, true, 1, GQ> : dequant_gemv_kernel<Q, false, 1, GQ>;
+  return off ? dequant_gemv_kernel<Q, true, kDqMaxBatch, GQ>
+             : dequant_gemv_kernel<Q, false, kDqMaxBatch, GQ>;
 }
 
-DqFn dq_kernel(int q, bool off, int mb) {
+template <int Q>
+DqFn dq_pick(bool off, int mb, bool gq) {
+  return gq ? dq_pick<Q, true>(off, mb) : dq_pick<Q, false>(off, mb);
+}
+
+DqFn dq_kernel(int q, bool off, int mb, bool gq) {
   switch (q) {
-    case 1: return dq_pick<1>(off, mb);
-    case 2: return dq_pick<2>(off, mb);
-    case 3: return dq_pick<3>(off, mb);
-    case 4: return dq_pick<4>(off, mb);
-    case 5: return dq_pick<5>(off, mb);
-    case 6: return dq_pick<6>(off, mb);
-    case 7: return dq_pick<7>(off, mb);
-    case 8: return dq_pick<8>(off, mb);
+    case 1: return dq_pick<1>(off, mb, gq);
+    case 2: return dq_pick<2>(off, mb, gq);
+    case 3: return dq_pick<3>(off, mb, gq);
+    case 4: return dq_pick<4>(off, mb, gq);
+    case 5: return dq_pick<5>(off, mb, gq);
+    case 6: return dq_pick<6>(off, mb, gq);
+    case 7: return dq_pick<7>(off, mb, gq);
+    case 8: return dq_pick<8>(off, mb, gq);
     default: return nullptr;
   }
 }
@@ -213,7 +240,7 @@ extern "C" int bcq_dequant_gemv(const lutgemm_shape* s, int32_t m, const void* d
     return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
   }
   const int mb = m == 1 ? 1 : kDqMaxBatch;
-  DqFn fn = dq_kernel((int)G.q, G.has_offset, mb);
+  DqFn fn = dq_kernel((int)G.q, G.has_offset, mb, G.g % 32 == 0);
   if (!fn) return LUTGEMM_ERR_INTERNAL;
   DqParams p{};
   p.bits = (const uint8_t*)d_bits;
