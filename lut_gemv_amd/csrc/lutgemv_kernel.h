@@ -26,6 +26,9 @@
 //    v_fma_mix_f32 (fp16 scale times fp32 sum into an fp32 accumulator);
 //  * each wave keeps the loads of the next one or two input tiles in flight (a
 //    ring of register sets filled by unconditional buffer loads);
+//  * at batch 1 the whole of x is staged in LDS once per workgroup (up to
+//    15360 inputs); from two batch rows on, the tables of two rows can be
+//    interleaved entry by entry so that one 64-bit read serves both rows;
 //  * when the input dimension is split over workgroups to fill the CUs, each
 //    writes fp32 partial sums with device-scope (write-through) stores; after
 //    its last item a workgroup waits for those stores to complete and counts
@@ -311,8 +314,8 @@ __device__ __forceinline__ void unpack8(const uint4 xr, float (&x)[8]) {
 }
 
 // Table of lane l's chunk into buffer `buf`: the entries whose high nibble
-// belongs to this wave (16/W high nibbles with 16 waves, two with 8 or 12; with
-// 12 waves only the first 8 build). Entry p = sum_t (bit t of p ? +x_t : -x_t).
+// belongs to this wave (one high nibble with 16 waves, two with 8). Entry
+// p = sum_t (bit t of p ? +x_t : -x_t).
 // The entries are visited in Gray-code order of their varying bits, so each is
 // the previous one plus or minus 2 x_t (one add, sign known at compile time);
 // the first is summed directly.
@@ -320,8 +323,7 @@ template <int W>
 __device__ __forceinline__ void build_table(float* lut, int buf, const LaneCtx& l, const uint4 xr) {
   constexpr int HPW = W == 16 ? 1 : 2;        // high nibbles per building wave
   constexpr int NB = HPW == 2 ? 5 : 4;        // pattern bits that vary within the wave
-  static_assert(W == 8 || W == 12 || W == 16, "8, 12 or 16 waves per workgroup");
-  if (W == 12 && l.wave >= 8) return;         // uniform over the wave
+  static_assert(W == 8 || W == 16, "8 or 16 waves per workgroup");
   float x[8];
   unpack8(xr, x);
   const int h0 = l.wave * HPW;                // first high nibble (even when HPW == 2)
@@ -634,7 +636,7 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // Each step (one batch row of one tile) looks up its table, builds the next
 // step's table in the other LDS buffer, and ends at the step's one barrier.
 // Q: sign planes; RPW: row tiles per wave; MC: batch rows per item; GQ: see
-// TileRegs; OFF: offset term; W: waves per workgroup (8, 12 or 16).
+// TileRegs; OFF: offset term; W: waves per workgroup (8 or 16).
 // XL (batch 1 only): x is staged whole in LDS at the start, and the tables are
 // built from there, instead of every wave loading each x tile from L2 (all
 // waves of all CUs reading the same lines).
