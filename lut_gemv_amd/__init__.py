@@ -304,11 +304,20 @@ class PackedBCQ:
                            torch.cuda.current_stream(self._ws.device).cuda_stream)
         return self._ws, self._ws.numel()
 
-    def __call__(self, x, out=None):
-        """y = W_hat x for fp16 x [m][K] on the device; returns fp16 y [m][N]."""
+    def _check_io(self, x, out):
         import torch
         if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != self.K:
             raise ValueError(f"x must be fp16 [m][{self.K}]")
+        if x.device != self.d_bits.device:
+            raise ValueError(f"x is on {x.device}, the weights on {self.d_bits.device}")
+        if out is not None and (out.dtype != torch.float16 or tuple(out.shape) != (x.shape[0], self.N)
+                                or out.device != x.device or not out.is_contiguous()):
+            raise ValueError(f"out must be a contiguous fp16 [{x.shape[0]}][{self.N}] tensor on {x.device}")
+
+    def __call__(self, x, out=None):
+        """y = W_hat x for fp16 x [m][K] on the device; returns fp16 y [m][N]."""
+        import torch
+        self._check_io(x, out)
         x = x.contiguous()
         m = x.shape[0]
         if out is None:
@@ -324,8 +333,7 @@ class PackedBCQ:
     def dequant(self, x, out=None):
         """The same product by the dequantizing comparison kernel (bcq_dequant_gemv)."""
         import torch
-        if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != self.K:
-            raise ValueError(f"x must be fp16 [m][{self.K}]")
+        self._check_io(x, out)
         x = x.contiguous()
         m = x.shape[0]
         if out is None:

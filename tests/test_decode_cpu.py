@@ -49,3 +49,20 @@ def test_unknown_model_and_bad_layers():
         decode.DecodeStack("gpt5", device="cpu")
     with pytest.raises(ValueError):
         decode.DecodeStack("llama7b", layers=0, device="cpu")
+
+
+def test_packed_call_checks_arguments():
+    """The binding rejects x or out of the wrong type, shape or device before any launch."""
+    import lut_gemv_amd as lg
+    import workloads
+    w = workloads.random_bcq(32, 512, 2, 128, seed=1)
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g, device="cpu")
+    good = torch.zeros((2, 512), dtype=torch.float16)
+    for bad in (torch.zeros((2, 512), dtype=torch.float32), torch.zeros((2, 256), dtype=torch.float16),
+                torch.zeros(512, dtype=torch.float16)):
+        with pytest.raises(ValueError):
+            pw(bad)
+    with pytest.raises(ValueError):
+        pw(good, out=torch.empty((2, 31), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        pw.dequant(good, out=torch.empty((2, 32), dtype=torch.float32))
