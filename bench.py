@@ -11,7 +11,7 @@ Prints ONE JSON line on stdout. ``value`` is the achieved algorithmic HBM rate
 (GB/s) over the wall-clock timed region; ``roofline.achieved`` is the same bytes
 over the average launch duration, from a HIP event pair recorded on the launch
 stream around the same region.
-``--gpus N`` with N > 1 exits: this build runs on one GPU.
+``--gpus N`` with N > 1 exits: the library has no multi-GPU path.
 """
 from __future__ import annotations
 
@@ -110,7 +110,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        msg = ("bench.py runs on one GPU only: this build has no multi-GPU path "
+        msg = ("bench.py runs on one GPU only: the library has no multi-GPU path "
                f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})")
         if int(os.environ.get("RANK", "0")) == 0:
             print(msg, file=sys.stderr, flush=True)
