@@ -31,18 +31,19 @@ __global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
 // ------------------------------------------------------------------ dispatch
 
 // ring: >= 3 asks for the deeper ring where an instance has one, 0 for the
-// default; xl: the variant with x staged in LDS (batch 1).
+// default; xl: the variant with x staged in LDS (batch 1); pr: paired tables;
+// ei: the early-issue ring of the x-in-LDS variant.
 KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring, bool xl,
-                     bool pr = false) {
+                     bool pr = false, bool ei = false) {
   switch (q) {
-    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl, pr);
-    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl, pr);
-    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring, xl, pr);
-    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring, xl, pr);
-    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring, xl, pr);
-    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring, xl, pr);
-    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring, xl, pr);
-    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring, xl, pr);
+    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring, xl, pr, ei);
     default: return nullptr;
   }
 }
@@ -53,24 +54,26 @@ struct Config {
   int ring;              // >= 3: the deeper ring; 0: the instance's default
   bool xl;               // x staged in LDS
   bool pr;               // paired tables (two batch rows per table entry)
+  bool ei;               // early-issue ring (x in LDS, two register sets)
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
 };
 
 struct TileOverride {
-  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1, pr = -1;
+  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1, pr = -1, ei = -1;
 };
 
-// Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR]]]]]]" (LUTGEMM_TILE);
+// Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR[,EI]]]]]]]" (LUTGEMM_TILE);
 // never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
 // (default: where possible). PR: 1 paired tables where an instance has them, 0
-// never (default: the dispatcher's choice).
+// never (default: the dispatcher's choice). EI: 1 the early-issue ring where
+// x is staged in LDS with the default ring, 0 never (the default).
 bool tile_override(TileOverride* o) {
   const char* e = getenv("LUTGEMM_TILE");
   if (!e || !*e) return false;
-  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring,
-                       &o->ri, &o->xl, &o->pr);
+  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring,
+                       &o->ri, &o->xl, &o->pr, &o->ei);
   return n >= 2;
 }
 
@@ -82,9 +85,11 @@ bool tile_override(TileOverride* o) {
 // Batch 1 with grouped scales (the HBM-bound case): when the matrix has
 // between 8 and 16 row tiles per CU, each CU takes one row block of
 // ceil(row tiles / CUs) row tiles over the whole input dimension, with 16
-// waves, x staged in LDS and a 2-deep ring (or, when x does not fit, x from
-// L2 and a 3-deep ring). All CUs then stream the same input tile window in
-// step (the best access pattern measured), with no split reduction.
+// waves, x staged in LDS and the early-issue 2-deep ring (or, when x does not
+// fit, x from L2 and a 3-deep ring). All CUs then stream the same input tile
+// window in step (the best access pattern measured), with no split reduction.
+// (The early-issue ring is slower where a CU has several items or the input
+// dimension is split, so it is used on this path only.)
 //
 // Otherwise a cost estimate charges each item its tiles, weighted by the row
 // tiles it covers and its batch rows (a tile step of 16 row tiles is one unit;
@@ -96,6 +101,8 @@ Config choose_config(const Geometry& G, int64_t m) {
   c.W = 0;   // stays 0 if no instance fits (reported as an internal error)
   c.ring = 0;
   c.xl = false;
+  c.pr = false;
+  c.ei = false;
   const int q = (int)G.q;
   const bool off = G.has_offset;
   // batch 1 with x small enough: stage it in LDS (16-wave instances)
@@ -112,6 +119,7 @@ Config choose_config(const Geometry& G, int64_t m) {
     c.RI = (int)ri1;
     c.ring = xl1 ? 0 : 3;
     c.xl = xl1;
+    c.ei = xl1 && pick_kernel(q, 1, 1, true, off, 16, 0, true, false, true) != nullptr;
     c.n_rb = (G.RT + ri1 - 1) / ri1;
     c.n_bg = 1;
     c.S = 1;
@@ -172,6 +180,8 @@ Config choose_config(const Geometry& G, int64_t m) {
     const bool xl = pr ? false
                     : o.xl < 0 ? xl_ok && pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, true)
                                : (o.xl > 0 && xl_ok);
+    const bool ei = o.ei > 0 && xl && o.ring < 3 &&
+                    pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, xl, pr, true) != nullptr;
     if (pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, xl, pr)) {
       c.W = w;
       c.RPW = o.rpw;
@@ -179,6 +189,7 @@ Config choose_config(const Geometry& G, int64_t m) {
       c.ring = o.ring;
       c.xl = xl;
       c.pr = pr;
+      c.ei = ei;
       c.RI = (o.ri >= 1 && o.ri <= c.W * c.RPW) ? o.ri : c.W * c.RPW;
       c.n_rb = (G.RT + c.RI - 1) / c.RI;
       c.n_bg = (m + c.MC - 1) / c.MC;
@@ -286,7 +297,8 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
       return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
     }
 
-    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr);
+    KernelFn fn =
+        pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr, c.ei);
     if (!fn) return LUTGEMM_ERR_INTERNAL;
     Params p{};
     p.bits = (const uint8_t*)d_bits;

@@ -643,7 +643,15 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // PR (two or more batch rows, grouped scales): paired tables in one buffer; each
 // tile takes, per pair of batch rows, a barrier, the pair's table build, a
 // barrier and the pair's lookups.
-template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL, bool PR = false>
+// EI (with XL and two register sets): a set is refilled with the tile two
+// ahead as soon as its lookups are done, instead of at the start of the next
+// step, so two tiles are in flight from the start (the staging of x and the
+// first table build overlap both). That loop leaves only after its second
+// step and issues its loads unconditionally: every path into the loop head
+// then has the same loads outstanding, and the compiler's wait counts before
+// the lookups stay exact (they would otherwise also wait for the tile ahead).
+template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL, bool PR = false,
+          bool EI = false>
 // The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
 // also the most that can ever run; saying so lets the scheduler use the
 // whole register budget to keep table lookups in flight.
@@ -651,6 +659,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) lutgemv_kernel(Params p) {
   static_assert(!XL || MC == 1, "x in LDS is for batch 1");
   static_assert(!PR || (GQ && !XL && MC % 2 == 0), "paired tables: grouped scales, even MC");
+  static_assert(!EI || (XL && NR == 2 && !PR), "early issue: x in LDS, two register sets");
   __shared__ float lut[2 * kLutWords];
   __shared__ uint4 xs[XL ? kXChunks : 1];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
@@ -681,6 +690,10 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
   if (!R[0].pos.live) return;
   load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[0]);
+  if constexpr (EI) {
+    R[1].pos = next_tile<RPW, MC, W>(p, l.wave, R[0].pos);
+    load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[1]);
+  }
 #pragma unroll
   for (int s = 1; s + 1 < NR; ++s) {
     R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
@@ -734,6 +747,28 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   int buf = 0;
   build_table<W>(lut, 0, l, xtile(R[0], 0));
   __syncthreads();
+  if constexpr (EI) {
+    for (;;) {
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        TR& cur = R[s];
+        TR& nxt = R[(s + 1) % NR];
+        const TilePos was = cur.pos;
+        if (was.live) lookups(l, 0, buf, lut, cur, acc);   // uniform over the workgroup
+        cur.pos = next_tile<RPW, MC, W>(p, l.wave, nxt.pos);
+        load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, cur);
+        if (was.live) {
+          if (nxt.pos.live) build_table<W>(lut, buf ^ 1, l, xtile(nxt, 0));
+          __syncthreads();
+          buf ^= 1;
+          if (was.kt + 1 == was.c.kt1) finish_item<RPW, MC>(p, l, was.c, acc);
+        }
+      }
+      if (!R[0].pos.live) break;
+    }
+    if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    return;
+  }
   bool done = false;
   while (!done) {
 #pragma unroll
@@ -812,9 +847,10 @@ constexpr int kRingPair =
 
 // ring 3 or 4 selects a deeper ring where an instance has one (16 waves); xl
 // the x-in-LDS variant (16 waves, batch 1, grouped scales); pr the paired
-// tables (grouped scales, even MC).
+// tables (grouped scales, even MC); ei the early-issue ring of the x-in-LDS
+// variant (default ring only).
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
-KernelFn kernel_or_null(int ring, bool xl, bool pr) {
+KernelFn kernel_or_null(int ring, bool xl, bool pr, bool ei) {
   if (pr) {
     if constexpr (GQ && kRingPair<Q, RPW, MC, OFF, W> > 0) {
       return xl ? nullptr
@@ -826,6 +862,7 @@ KernelFn kernel_or_null(int ring, bool xl, bool pr) {
   if constexpr (kInstantiated<Q, RPW, MC, GQ, OFF, W>) {
     if constexpr (W == 16 && MC == 1 && GQ) {
       if (xl) {
+        if (ei && ring < 3) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 2, true, false, true>;
         if constexpr (kFits16<Q, RPW, MC, GQ, OFF, W, true, 4>) {
           if (ring == 4) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 4, true>;
         }
@@ -843,52 +880,54 @@ KernelFn kernel_or_null(int ring, bool xl, bool pr) {
   } else {
     (void)ring;
     (void)xl;
+    (void)ei;
     return nullptr;
   }
 }
 
 template <int Q, int RPW, int MC, int W>
-KernelFn pick_flags(bool gq, bool off, int ring, bool xl, bool pr) {
+KernelFn pick_flags(bool gq, bool off, int ring, bool xl, bool pr, bool ei) {
   if (gq)
-    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl, pr)
-               : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl, pr);
-  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring, xl, pr)
-             : kernel_or_null<Q, RPW, MC, false, false, W>(ring, xl, pr);
+    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl, pr, ei)
+               : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl, pr, ei);
+  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring, xl, pr, ei)
+             : kernel_or_null<Q, RPW, MC, false, false, W>(ring, xl, pr, ei);
 }
 
 template <int Q, int W>
-KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool pr) {
+KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool pr, bool ei) {
   if (mc == 1) {
-    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl, pr);
-    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring, xl, pr);
+    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl, pr, ei);
+    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring, xl, pr, ei);
   } else if (mc == 2) {
-    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring, xl, pr);
-    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring, xl, pr);
+    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring, xl, pr, ei);
+    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring, xl, pr, ei);
   } else if (mc == 4) {
-    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring, xl, pr);
-    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring, xl, pr);
+    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring, xl, pr, ei);
+    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring, xl, pr, ei);
   }
   return nullptr;
 }
 
 // The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
 // item, scale groups aligned to 32 inputs (gq), an offset term (off), w waves
-// per workgroup, ring depth (0 default, >= 3 deeper), x in LDS (xl) and paired
-// tables (pr), or nullptr if none is built.
+// per workgroup, ring depth (0 default, >= 3 deeper), x in LDS (xl), paired
+// tables (pr) and the early-issue ring (ei), or nullptr if none is built.
 template <int Q>
-KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, bool pr) {
-  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl, pr);
-  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl, pr);
+KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, bool pr,
+                      bool ei) {
+  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl, pr, ei);
+  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl, pr, ei);
   return nullptr;
 }
 
-extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, bool);
-extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, bool);
-extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool, bool);
-extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool, bool);
-extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool, bool);
-extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool, bool);
-extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool, bool);
-extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool, bool);
+extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool, bool, bool);
 
 }  // namespace lutgemm

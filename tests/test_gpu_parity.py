@@ -259,6 +259,26 @@ def test_paired_tables_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# "RPW,S,W,MC,ring,RI,XL,PR,EI": x in LDS with the early-issue ring (EI = 1), forced
+# onto single-item, split and many-item launches, and the plain ring beside it (EI = 0)
+@pytest.mark.parametrize("tile", ["1,1,16,1,0,12,1,0,1", "1,1,16,1,0,12,1,0,0", "1,3,16,1,0,5,1,0,1",
+                                  "2,2,16,1,0,20,1,0,1"])
+@pytest.mark.parametrize("N,K,q,g,m,off", [
+    (3000, 4128, 3, 32, 1, True),      # ragged rows and input tiles
+    (2000, 12288, 3, 128, 1, False),
+    (777, 15360, 4, 64, 1, True),      # the largest x staged in LDS
+    (64, 512, 1, 32, 1, False),        # one input tile: fewer tiles than ring steps
+])
+def test_early_issue_ring_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + K + q, with_offset=off,
+                             name=f"early_issue_{N}x{K}q{q}g{g}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", tile)
+    _say(f"early-issue ring {tile}: N={N} K={K} q={q} g={g} offset={off}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
 def test_workspace_reuse_across_shapes():
     """One workspace serves a large split call, then a smaller one, then the large again."""
     big = workloads.random_bcq(8192, 12288, 3, 128, m=1, seed=6)
