@@ -25,7 +25,9 @@
 //    (g % 32 == 0) the four entries of a row are summed and scaled once with a
 //    v_fma_mix_f32 (fp16 scale times fp32 sum into an fp32 accumulator);
 //  * each wave keeps the loads of the next one or two input tiles in flight (a
-//    ring of register sets filled by unconditional buffer loads);
+//    ring of register sets filled by unconditional buffer loads); on the
+//    batch-1 launch that streams one row block per CU, a set is refilled as
+//    soon as its lookups are done, so two tiles are in flight from the start;
 //  * at batch 1 the whole of x is staged in LDS once per workgroup (up to
 //    15360 inputs); from two batch rows on, the tables of two rows can be
 //    interleaved entry by entry so that one 64-bit read serves both rows;
