@@ -687,6 +687,11 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     const auto xrs = make_rsrc(p.x, (uint32_t)p.K * 2u);
 #pragma unroll
     for (int j = 0; j < NX; ++j) xr[j] = load16(xrs, ((uint32_t)threadIdx.x + (uint32_t)(j * W * 64)) * 16u);
+    // A compiler-only barrier: without it the loads of x are sunk below the
+    // exit and the item arithmetic that follow (two integer divisions and a
+    // second round of argument loads), and the cold fetch of x, the first
+    // thing every workgroup waits for, starts that much later.
+    asm volatile("" ::: "memory");
   }
   TR R[NR];
   R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
