@@ -105,12 +105,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // The range check covers voff (per lane) plus soff (scalar): a descriptor
 // whose num_records is soff + n admits exactly voff < n.
+// NT sets the non-temporal cache policy bit (for data read once per product,
+// so that it does not evict what is read again, such as x).
+template <bool NT = false>
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, uni(soff), 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, uni(soff), NT ? 2 : 0));
 }
 
+template <bool NT = false>
 __device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, uni(soff), 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, uni(soff), NT ? 2 : 0));
 }
 
 // ------------------------------------------------------------------ work items
@@ -235,7 +239,10 @@ __device__ __forceinline__ void tile_group_offsets(const Params& p, LaneCtx& l) 
 
 // Issue the loads of the tile at T.pos (all of them unconditional; activations
 // first, so the table build waits only for those). A dead position gives
-// zero-length ranges: the instructions issue but touch no memory.
+// zero-length ranges: the instructions issue but touch no memory. With x in LDS
+// (batch 1) every weight byte is read once per product, and its loads are
+// non-temporal; with several batch groups the groups re-read the same weights,
+// which the caches then serve.
 template <int Q, int RPW, int MC, bool GQ, bool OFF, bool XL>
 __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
                                           TileRegs<Q, RPW, MC, GQ, OFF>& T) {
@@ -263,7 +270,7 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int q = 0; q < Q; ++q)
-      T.bw[i][q] = load16(br, (uint32_t)(i * kTileBytes + q * kChunkTile * kRowTile) + l.block, bs);
+      T.bw[i][q] = load16<XL>(br, (uint32_t)(i * kTileBytes + q * kChunkTile * kRowTile) + l.block, bs);
   const int g_first = group_of(p, k0);
   const uint32_t g_span = (uint32_t)min(p.G - g_first, p.g_span);
   // byte offset of the scales (offsets) of each chunk this lane visits
@@ -293,7 +300,7 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
     for (int k = 0; k < NV; ++k) {
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const uint2 v = load8(ar, aoff[k] + (uint32_t)(q * 32), blk * (32u * Q));
+        const uint2 v = load8<XL>(ar, aoff[k] + (uint32_t)(q * 32), blk * (32u * Q));
         T.aw[i][(k * Q + q) * 2] = v.x;
         T.aw[i][(k * Q + q) * 2 + 1] = v.y;
       }
@@ -302,7 +309,7 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
       const auto orr = make_rsrc(p.offset, on ? (blk + g_span) * 32u : 0u);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const uint2 v = load8(orr, ooff[k], blk * 32u);
+        const uint2 v = load8<XL>(orr, ooff[k], blk * 32u);
         T.ow[i][2 * k] = v.x;
         T.ow[i][2 * k + 1] = v.y;
       }
