@@ -240,9 +240,11 @@ __device__ __forceinline__ void tile_group_offsets(const Params& p, LaneCtx& l) 
 // Issue the loads of the tile at T.pos (all of them unconditional; activations
 // first, so the table build waits only for those). A dead position gives
 // zero-length ranges: the instructions issue but touch no memory. With x in LDS
-// (batch 1) every weight byte is read once per product, and its loads are
-// non-temporal; with several batch groups the groups re-read the same weights,
-// which the caches then serve.
+// (batch 1) every sign byte is read once per product, each load consuming whole
+// lines, and those loads are non-temporal. Scale and offset loads stay ordinary:
+// the loads of the planes share their lines, and a non-temporal line can be
+// gone before the next plane's load. With several batch groups the groups
+// re-read the same weights, which the caches then serve.
 template <int Q, int RPW, int MC, bool GQ, bool OFF, bool XL>
 __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
                                           TileRegs<Q, RPW, MC, GQ, OFF>& T) {
@@ -300,7 +302,7 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
     for (int k = 0; k < NV; ++k) {
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const uint2 v = load8<XL>(ar, aoff[k] + (uint32_t)(q * 32), blk * (32u * Q));
+        const uint2 v = load8(ar, aoff[k] + (uint32_t)(q * 32), blk * (32u * Q));
         T.aw[i][(k * Q + q) * 2] = v.x;
         T.aw[i][(k * Q + q) * 2 + 1] = v.y;
       }
@@ -309,7 +311,7 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
       const auto orr = make_rsrc(p.offset, on ? (blk + g_span) * 32u : 0u);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const uint2 v = load8<XL>(orr, ooff[k], blk * 32u);
+        const uint2 v = load8(orr, ooff[k], blk * 32u);
         T.ow[i][2 * k] = v.x;
         T.ow[i][2 * k + 1] = v.y;
       }
