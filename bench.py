@@ -101,7 +101,8 @@ def main():
                     help="lut: the LUT-GEMV (the product); dequant: the dequantizing comparison "
                          "kernel on the same packed data")
     ap.add_argument("--rotate", type=int, default=0,
-                    help="distinct weight copies cycled through (0: enough for >= 1 GiB)")
+                    help="distinct weight copies cycled through (0: enough for >= 4 GiB, at "
+                         "most 4096 copies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed region, copy MIB MiB device to device 5 times "
@@ -138,7 +139,13 @@ def main():
     nbytes = algorithmic_bytes(w.N, w.K, w.q, w.g, w.m, has_off)
     weight_bytes = pw0.d_bits.numel() + 2 * pw0.d_alpha.numel() + \
         (2 * pw0.d_offset.numel() if has_off else 0)
-    R = args.rotate if args.rotate > 0 else max(1, -(-(1 << 30) // weight_bytes))
+    # Enough distinct copies that no part of the weights can stay in the 256 MB
+    # last-level cache between launches: the sign planes are read with a
+    # non-temporal hint, so the scales of all copies (11% of the bytes at g=128)
+    # must by themselves be well past the cache's size. 4 GiB of weights does
+    # that at every group size here; tiny shapes, which are launch-bound, stop
+    # at 4096 copies.
+    R = args.rotate if args.rotate > 0 else min(4096, max(1, -(-(4 << 30) // weight_bytes)))
     copies = [pw0]
     for _ in range(R - 1):
         copies.append(lg.PackedBCQ(w.N, w.K, w.q, w.g, pw0.d_bits.clone(), pw0.d_alpha.clone(),
