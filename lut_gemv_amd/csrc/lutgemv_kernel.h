@@ -28,6 +28,8 @@
 //    ring of register sets filled by unconditional buffer loads); on the
 //    batch-1 launch that streams one row block per CU, a set is refilled as
 //    soon as its lookups are done, so two tiles are in flight from the start;
+//    at batch 1 the sign planes, read once per product, are loaded with the
+//    non-temporal cache hint so that they do not evict what is read again;
 //  * at batch 1 the whole of x is staged in LDS once per workgroup (up to
 //    15360 inputs); from two batch rows on, the tables of two rows can be
 //    interleaved entry by entry so that one 64-bit read serves both rows;
@@ -698,8 +700,8 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     for (int j = 0; j < NX; ++j) xr[j] = load16(xrs, ((uint32_t)threadIdx.x + (uint32_t)(j * W * 64)) * 16u);
     // A compiler-only barrier: without it the loads of x are sunk below the
     // exit and the item arithmetic that follow (two integer divisions and a
-    // second round of argument loads), and the cold fetch of x, the first
-    // thing every workgroup waits for, starts that much later.
+    // second round of argument loads), and the fetch of x, the first thing
+    // every workgroup waits for, starts that much later.
     asm volatile("" ::: "memory");
   }
   TR R[NR];
