@@ -32,18 +32,19 @@ __global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
 
 // ring: >= 3 asks for the deeper ring where an instance has one, 0 for the
 // default; xl: the variant with x staged in LDS (batch 1); pr: paired tables;
-// ei: the early-issue ring of the x-in-LDS variant.
+// ei: the early-issue ring of the x-in-LDS variant; once: read-once
+// (non-temporal) sign-plane loads at batch 1 without x in LDS.
 KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring, bool xl,
-                     bool pr = false, bool ei = false) {
+                     bool pr = false, bool ei = false, bool once = false) {
   switch (q) {
-    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl, pr, ei);
-    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl, pr, ei);
-    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring, xl, pr, ei);
-    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring, xl, pr, ei);
-    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring, xl, pr, ei);
-    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring, xl, pr, ei);
-    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring, xl, pr, ei);
-    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring, xl, pr, ei);
+    case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
+    case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
+    case 3: return kernels_of_q<3>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
+    case 4: return kernels_of_q<4>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
+    case 5: return kernels_of_q<5>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
+    case 6: return kernels_of_q<6>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
+    case 7: return kernels_of_q<7>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
+    case 8: return kernels_of_q<8>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
     default: return nullptr;
   }
 }
@@ -55,6 +56,7 @@ struct Config {
   bool xl;               // x staged in LDS
   bool pr;               // paired tables (two batch rows per table entry)
   bool ei;               // early-issue ring (x in LDS, two register sets)
+  bool once;             // batch 1 without x in LDS: non-temporal sign-plane loads
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
@@ -103,6 +105,7 @@ Config choose_config(const Geometry& G, int64_t m) {
   c.xl = false;
   c.pr = false;
   c.ei = false;
+  c.once = false;
   const int q = (int)G.q;
   const bool off = G.has_offset;
   // batch 1 with x small enough: stage it in LDS (16-wave instances)
@@ -198,6 +201,12 @@ Config choose_config(const Geometry& G, int64_t m) {
   }
   if (c.S < 1) c.S = 1;
   if (c.n_rb * c.n_bg > kMaxCounters) c.S = 1;   // counters live in a fixed region
+  // batch 1 without x in LDS: each sign byte is still read once per product
+  // (where a read-once instance exists for the choice, it differs from the
+  // ordinary one)
+  c.once = m == 1 && !c.xl && !c.pr && c.MC == 1 &&
+           pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, c.ring, false, false, false, true) !=
+               pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, c.ring, false, false, false, false);
   c.ws_bytes = c.S > 1 ? kCounterBytes + (size_t)c.S * (size_t)m * (size_t)G.Npad * sizeof(float) : 0;
   return c;
 }
@@ -297,8 +306,8 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
       return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
     }
 
-    KernelFn fn =
-        pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr, c.ei);
+    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr,
+                              c.ei, c.once);
     if (!fn) return LUTGEMM_ERR_INTERNAL;
     Params p{};
     p.bits = (const uint8_t*)d_bits;

@@ -241,13 +241,13 @@ __device__ __forceinline__ void tile_group_offsets(const Params& p, LaneCtx& l) 
 
 // Issue the loads of the tile at T.pos (all of them unconditional; activations
 // first, so the table build waits only for those). A dead position gives
-// zero-length ranges: the instructions issue but touch no memory. With x in LDS
-// (batch 1) every sign byte is read once per product, each load consuming whole
+// zero-length ranges: the instructions issue but touch no memory. NT: every
+// sign byte is read once per product (batch 1), each load consuming whole
 // lines, and those loads are non-temporal. Scale and offset loads stay ordinary:
 // the loads of the planes share their lines, and a non-temporal line can be
 // gone before the next plane's load. With several batch groups the groups
 // re-read the same weights, which the caches then serve.
-template <int Q, int RPW, int MC, bool GQ, bool OFF, bool XL>
+template <int Q, int RPW, int MC, bool GQ, bool OFF, bool XL, bool NT>
 __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
                                           TileRegs<Q, RPW, MC, GQ, OFF>& T) {
   constexpr uint32_t kTileBytes = Q * kChunkTile * kRowTile;
@@ -274,7 +274,7 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int q = 0; q < Q; ++q)
-      T.bw[i][q] = load16<XL>(br, (uint32_t)(i * kTileBytes + q * kChunkTile * kRowTile) + l.block, bs);
+      T.bw[i][q] = load16<NT>(br, (uint32_t)(i * kTileBytes + q * kChunkTile * kRowTile) + l.block, bs);
   const int g_first = group_of(p, k0);
   const uint32_t g_span = (uint32_t)min(p.G - g_first, p.g_span);
   // byte offset of the scales (offsets) of each chunk this lane visits
@@ -663,8 +663,10 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // step and issues its loads unconditionally: every path into the loop head
 // then has the same loads outstanding, and the compiler's wait counts before
 // the lookups stay exact (they would otherwise also wait for the tile ahead).
+// ONCE (batch 1 without x in LDS): each sign byte is read once per product, and
+// its loads are non-temporal as they are with XL.
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL, bool PR = false,
-          bool EI = false>
+          bool EI = false, bool ONCE = false>
 // The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
 // also the most that can ever run; saying so lets the scheduler use the
 // whole register budget to keep table lookups in flight.
@@ -673,6 +675,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   static_assert(!XL || MC == 1, "x in LDS is for batch 1");
   static_assert(!PR || (GQ && !XL && MC % 2 == 0), "paired tables: grouped scales, even MC");
   static_assert(!EI || (XL && NR == 2 && !PR), "early issue: x in LDS, two register sets");
+  static_assert(!ONCE || (!XL && !PR && MC == 1), "read-once loads: batch 1 without x in LDS");
   __shared__ float lut[2 * kLutWords];
   __shared__ uint4 xs[XL ? kXChunks : 1];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
@@ -708,24 +711,24 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
   if constexpr (XL) {
     if (!R[0].pos.live) return;
-    load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[0]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[0]);
   } else {
     // The first tile's loads go ahead of the exit (a dead position touches no
     // memory), and the barrier keeps them there, so the buffer addresses they
     // need are fetched with the other kernel arguments in one round instead of
     // a third round after the exit.
-    load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[0]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[0]);
     asm volatile("" ::: "memory");
     if (!R[0].pos.live) return;
   }
   if constexpr (EI) {
     R[1].pos = next_tile<RPW, MC, W>(p, l.wave, R[0].pos);
-    load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[1]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[1]);
   }
 #pragma unroll
   for (int s = 1; s + 1 < NR; ++s) {
     R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
-    load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, R[s]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[s]);
   }
   if constexpr (XL) {   // chunk c of x at xs[c], for the KT input tiles (zero past K)
     const int nchunks = p.KT * kChunkTile;
@@ -754,7 +757,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
           TR& nxt = R[(s + 1) % NR];
           TR& pre = R[(s + NR - 1) % NR];
           pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
-          load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, pre);
+          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
 #pragma unroll
           for (int h = 0; h < MC / 2; ++h) {
             if (2 * h < cur.pos.c.rows_here) {  // uniform over the workgroup
@@ -784,7 +787,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         const TilePos was = cur.pos;
         if (was.live) lookups(l, 0, buf, lut, cur, acc);   // uniform over the workgroup
         cur.pos = next_tile<RPW, MC, W>(p, l.wave, nxt.pos);
-        load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, cur);
+        load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, cur);
         if (was.live) {
           if (nxt.pos.live) build_table<W>(lut, buf ^ 1, l, xtile(nxt, 0));
           __syncthreads();
@@ -806,7 +809,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         TR& nxt = R[(s + 1) % NR];
         TR& pre = R[(s + NR - 1) % NR];
         pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
-        load_tile<Q, RPW, MC, GQ, OFF, XL>(p, l, pre);
+        load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
 #pragma unroll
         for (int r = 0; r < MC; ++r) {
           if (r < cur.pos.c.rows_here) {  // uniform over the workgroup
@@ -876,9 +879,10 @@ constexpr int kRingPair =
 // ring 3 or 4 selects a deeper ring where an instance has one (16 waves); xl
 // the x-in-LDS variant (16 waves, batch 1, grouped scales); pr the paired
 // tables (grouped scales, even MC); ei the early-issue ring of the x-in-LDS
-// variant (default ring only).
+// variant (default ring only); once the read-once (non-temporal) sign-plane
+// loads of the 16-wave batch-1 instances without x in LDS.
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
-KernelFn kernel_or_null(int ring, bool xl, bool pr, bool ei) {
+KernelFn kernel_or_null(int ring, bool xl, bool pr, bool ei, bool once) {
   if (pr) {
     if constexpr (GQ && kRingPair<Q, RPW, MC, OFF, W> > 0) {
       return xl ? nullptr
@@ -900,8 +904,14 @@ KernelFn kernel_or_null(int ring, bool xl, bool pr, bool ei) {
         return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 2, true>;
       }
       if constexpr (kFits16<Q, RPW, MC, GQ, OFF, W, false, 3>) {
-        if (ring >= 3) return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3, false>;
+        if (ring >= 3) {
+          return once ? lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3, false, false, false, true>
+                      : lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, 3, false>;
+        }
       }
+      if (once && !xl)
+        return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRing<Q, RPW, MC, GQ, OFF, W>, false, false,
+                              false, true>;
     }
     if (xl) return nullptr;
     return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRing<Q, RPW, MC, GQ, OFF, W>, false>;
@@ -909,30 +919,32 @@ KernelFn kernel_or_null(int ring, bool xl, bool pr, bool ei) {
     (void)ring;
     (void)xl;
     (void)ei;
+    (void)once;
     return nullptr;
   }
 }
 
 template <int Q, int RPW, int MC, int W>
-KernelFn pick_flags(bool gq, bool off, int ring, bool xl, bool pr, bool ei) {
+KernelFn pick_flags(bool gq, bool off, int ring, bool xl, bool pr, bool ei, bool once) {
   if (gq)
-    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl, pr, ei)
-               : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl, pr, ei);
-  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring, xl, pr, ei)
-             : kernel_or_null<Q, RPW, MC, false, false, W>(ring, xl, pr, ei);
+    return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl, pr, ei, once)
+               : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl, pr, ei, once);
+  return off ? kernel_or_null<Q, RPW, MC, false, true, W>(ring, xl, pr, ei, once)
+             : kernel_or_null<Q, RPW, MC, false, false, W>(ring, xl, pr, ei, once);
 }
 
 template <int Q, int W>
-KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool pr, bool ei) {
+KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool pr, bool ei,
+                     bool once) {
   if (mc == 1) {
-    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl, pr, ei);
-    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring, xl, pr, ei);
+    if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl, pr, ei, once);
+    if (rpw == 1) return pick_flags<Q, 1, 1, W>(gq, off, ring, xl, pr, ei, once);
   } else if (mc == 2) {
-    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring, xl, pr, ei);
-    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring, xl, pr, ei);
+    if (rpw == 2) return pick_flags<Q, 2, 2, W>(gq, off, ring, xl, pr, ei, once);
+    if (rpw == 1) return pick_flags<Q, 1, 2, W>(gq, off, ring, xl, pr, ei, once);
   } else if (mc == 4) {
-    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring, xl, pr, ei);
-    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring, xl, pr, ei);
+    if (rpw == 2) return pick_flags<Q, 2, 4, W>(gq, off, ring, xl, pr, ei, once);
+    if (rpw == 1) return pick_flags<Q, 1, 4, W>(gq, off, ring, xl, pr, ei, once);
   }
   return nullptr;
 }
@@ -940,22 +952,23 @@ KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool
 // The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
 // item, scale groups aligned to 32 inputs (gq), an offset term (off), w waves
 // per workgroup, ring depth (0 default, >= 3 deeper), x in LDS (xl), paired
-// tables (pr) and the early-issue ring (ei), or nullptr if none is built.
+// tables (pr), the early-issue ring (ei) and read-once sign-plane loads (once),
+// or nullptr if none is built.
 template <int Q>
 KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, bool pr,
-                      bool ei) {
-  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl, pr, ei);
-  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl, pr, ei);
+                      bool ei, bool once) {
+  if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl, pr, ei, once);
+  if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl, pr, ei, once);
   return nullptr;
 }
 
-extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, bool, bool);
-extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, bool, bool);
-extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool, bool, bool);
-extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool, bool, bool);
-extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool, bool, bool);
-extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool, bool, bool);
-extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool, bool, bool);
-extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool, bool, bool);
+extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool, bool, bool, bool);
 
 }  // namespace lutgemm

@@ -7,5 +7,5 @@
 #endif
 
 namespace lutgemm {
-template KernelFn kernels_of_q<LUTGEMM_Q>(int, int, bool, bool, int, int, bool, bool, bool);
+template KernelFn kernels_of_q<LUTGEMM_Q>(int, int, bool, bool, int, int, bool, bool, bool, bool);
 }  // namespace lutgemm

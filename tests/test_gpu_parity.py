@@ -279,6 +279,21 @@ def test_early_issue_ring_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# batch 1 with x too long for LDS: read-once (non-temporal) sign-plane loads, in the
+# dispatcher's configuration and in forced ones (split, two row tiles per wave, 3-deep ring)
+@pytest.mark.parametrize("tile", ["", "1,3,16,1,0,16", "2,2,16,1,0,20", "1,4,16,1,3,12"])
+@pytest.mark.parametrize("N,K,q,g,off", [(2000, 20480, 3, 128, False), (333, 16896, 4, 64, True)])
+def test_read_once_batch1_long_x_all_outputs(monkeypatch, tile, N, K, q, g, off):
+    w = workloads.random_bcq(N, K, q, g, m=1, seed=N + K, with_offset=off,
+                             name=f"read_once_{N}x{K}q{q}g{g}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    if tile:
+        monkeypatch.setenv("LUTGEMM_TILE", tile)
+    _say(f"read-once loads {tile or 'default'}: N={N} K={K} q={q} g={g} offset={off}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE", raising=False)
+
+
 def test_workspace_reuse_across_shapes():
     """One workspace serves a large split call, then a smaller one, then the large again."""
     big = workloads.random_bcq(8192, 12288, 3, 128, m=1, seed=6)
