@@ -79,6 +79,7 @@ struct Params {
   int g_shift;              // log2(g) when g is a power of two, else -1
   int g_span;               // most scale groups one input tile touches
   int g_tile;               // 1 if g divides 512: every input tile starts a group
+  int xcd_bg;               // 1: the batch groups of one weight block are 8 items apart
 };
 
 __device__ __forceinline__ float h2f(uint32_t word, int hi) {
@@ -140,16 +141,37 @@ struct TilePos {
   bool live;              // false past the workgroup's last item: loads touch no memory
 };
 
+// Work item -> (batch group, split, weight block = row block + n_rb * split).
+// Normally the row block varies fastest, then the split, then the batch group.
+// With xcd_bg (several batch groups, items per batch group a multiple of 8) the
+// batch groups of one weight block are 8 items apart instead: workgroups b and
+// b + 8 run on the same XCD (dispatch goes round-robin over the 8 XCDs), so the
+// batch groups that re-read one block's weights run at the same time and share
+// that XCD's L2.
+__device__ __forceinline__ void decode_item(const Params& p, int item, int& bg, int& split,
+                                            int& rb) {
+  const int per = p.n_rb * p.S;
+  int w;
+  if (p.xcd_bg) {
+    const int j = item >> 3;
+    const int y = j / p.n_bg;
+    bg = j - y * p.n_bg;
+    w = (item & 7) + 8 * y;
+  } else {
+    bg = item / per;
+    w = item - bg * per;
+  }
+  split = w / p.n_rb;
+  rb = w - split * p.n_rb;
+}
+
 template <int RPW, int MC, int W>
 __device__ __forceinline__ TilePos first_tile(const Params& p, int wave, int item) {
   TilePos t;
   t.c.item = item;
   t.live = item < p.n_items;
-  const int per = p.n_rb * p.S;
-  const int bg = item / per;
-  const int rem = item - bg * per;
-  t.c.split = rem / p.n_rb;
-  const int rb = rem - t.c.split * p.n_rb;
+  int bg, rb;
+  decode_item(p, item, bg, t.c.split, rb);
   t.kt = t.c.split * p.KT / p.S;
   t.c.kt1 = (t.c.split + 1) * p.KT / p.S;
   t.c.rt_first = rb * p.ri + wave * RPW;
@@ -592,14 +614,13 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
   const int kRows = p.ri * kRowTile;   // rows per row block
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt = expcnt = lgkmcnt = 0: own stores complete
   __syncthreads();
-  const int per = p.n_rb * p.S;
   const int n_mine = (p.n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   for (int j0 = 0; j0 < n_mine; j0 += kThreads) {
     const int nj = min(kThreads, n_mine - j0);
     if ((int)threadIdx.x < nj) {
       const int item = (int)blockIdx.x + (j0 + (int)threadIdx.x) * (int)gridDim.x;
-      const int bg = item / per;
-      const int rb = (item - bg * per) % p.n_rb;
+      int bg, split, rb;
+      decode_item(p, item, bg, split, rb);
       uint32_t* ctr = p.counters + (size_t)bg * p.n_rb + rb;
       const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = prev == (uint32_t)(p.S - 1);
@@ -615,8 +636,8 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
       if (item < 0) continue;
       const int rem = idx - j * per_item;
       const int r = rem / kRows;
-      const int bg = item / per;
-      const int rb = (item - bg * per) % p.n_rb;
+      int bg, split, rb;
+      decode_item(p, item, bg, split, rb);
       const int row = rb * kRows + (rem - r * kRows);
       const int rr = bg * MC + r;
       if (row >= p.N || rr >= p.m) continue;

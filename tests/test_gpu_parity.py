@@ -294,6 +294,20 @@ def test_read_once_batch1_long_x_all_outputs(monkeypatch, tile, N, K, q, g, off)
     monkeypatch.delenv("LUTGEMM_TILE", raising=False)
 
 
+# 2 or 3 batch groups of one-row items, items per batch group a multiple of 8: the batch
+# groups of one weight block run side by side on one XCD, split reductions included
+@pytest.mark.parametrize("tile,N,K,m", [("1,3,16,1,0,16", 2048, 12288, 3), ("1,2,16,1,0,16", 1000, 8192, 2),
+                                        ("1,1,16,1,0,16", 2048, 4096, 2), ("2,4,16,1,0,32", 4096, 4096, 3)])
+def test_xcd_grouped_batch_groups_all_outputs(monkeypatch, tile, N, K, m):
+    w = workloads.random_bcq(N, K, 3, 128, m=m, seed=N + K + m, with_offset=True,
+                             name=f"xcd_groups_{N}x{K}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", tile)
+    _say(f"batch groups on one XCD {tile}: N={N} K={K} m={m}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
 def test_workspace_reuse_across_shapes():
     """One workspace serves a large split call, then a smaller one, then the large again."""
     big = workloads.random_bcq(8192, 12288, 3, 128, m=1, seed=6)
