@@ -337,7 +337,7 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     p.n_bg = (int)c.n_bg;
     // Batch groups of one weight block side by side on one XCD (see decode_item):
     // measured 0.7-1.8 us faster at 2 and 3 batch groups of one-row items; at 4
-    // it moved by -0.8..+0.3 us between boxes, and with paired tables at 4..16
+    // it moved by -0.8..+0.3 us from one machine to another, and with paired tables at 4..16
     // groups it was slower (each round then streams few distinct blocks).
     p.xcd_bg = (!c.pr && c.n_bg > 1 && c.n_bg <= 3 && (c.n_rb * c.S) % 8 == 0) ? 1 : 0;
     const int64_t items = c.n_rb * c.n_bg * c.S;
