@@ -8,9 +8,16 @@ with fp16 scales per group of 128, batch 1, fp16 x ~ N(0,1) (synthetic: the
 pages' trained weights are not used).
 
 Prints ONE JSON line on stdout. ``value`` is the achieved algorithmic HBM rate
-(GB/s) over the wall-clock timed region; ``roofline.achieved`` is the same bytes
+(GB/s) over the wall-clock timed region; ``roofline.achieved`` is the same work
 over the average launch duration, from a HIP event pair recorded on the launch
-stream around the same region.
+stream around the same region. ``roofline.bound`` is the larger of the two
+algorithmic floors of the workload: HBM bytes at 8 TB/s, or fp32 arithmetic
+(two flops per lookup, the tables built once) at the non-packed fp32 vector
+rate of 78.6 TFLOP/s.
+Before the ``--warmup`` launches, untimed launches run for at least
+``--settle-s`` seconds and one full pass over the rotating weight copies, so
+that clocks and caches are in their steady state however short the warm-up is
+(reported as ``settle``).
 ``--gpus N`` with N > 1 exits: the library has no multi-GPU path.
 """
 from __future__ import annotations
@@ -27,6 +34,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("µs/GEMV + achieved HBM GB/s, K=12288 N=49152 3-bit BCQ g=128, batch 1")
 HBM_PEAK_GBS = 8000.0
+# fp32 vector arithmetic without packed math: one wave64 instruction per clock
+# per compute unit, 256 CUs at 2.4 GHz, an FMA counting two flops (the 157.3
+# TFLOP/s figure counts packed FMAs, which this code does not use)
+ALU_PEAK_TFLOPS = 256 * 2.4e9 * 64 * 2 / 1e12
 KERNEL_SRCS = [os.path.join(ROOT, "lut_gemv_amd", "csrc", f)
                for f in ("lutgemv_kernel.h", "lutgemv_q.hip", "lutgemv.hip", "layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lutgemv_traffic.json")
@@ -43,6 +54,16 @@ def algorithmic_bytes(N, K, q, g, m, has_offset):
     if has_offset:
         b += 2 * N * G
     return b
+
+
+def algorithmic_flops(N, K, q, g, m, has_offset):
+    """fp32 operations the method must do: one multiply-add per lookup (m*N*q*K/8
+    lookups), each chunk's 256-entry table built once per batch row (one add per
+    entry), and one multiply-add per (batch row, row, group) for the offset."""
+    f = 2 * m * N * q * (K // 8) + m * (K // 8) * 256
+    if has_offset:
+        f += 2 * m * N * (K // g)
+    return f
 
 
 def kernel_hash():
@@ -67,22 +88,67 @@ def stored_traffic(workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of rows, one BLAS thread, scaled to a full product."""
+def cpu_baseline(w, threads, budget_s):
+    """The fp64 oracle on a bounded sample of rows, scaled to a full product.
+
+    ``threads`` workers each run the oracle (unchanged) on their own blocks of
+    256 rows with one BLAS thread, until ``budget_s`` seconds have passed or
+    every row is done. Returns (seconds per full product, rows done, elapsed)."""
     import numpy as np
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
-    rows_done = 0
-    t0 = time.perf_counter()
     block = 256
+    starts = list(range(0, w.N, block))
+    t0 = time.perf_counter()
+
+    def one(r0):
+        if time.perf_counter() - t0 >= budget_s:
+            return 0
+        rows = np.arange(r0, min(w.N, r0 + block))
+        oracle.gemv(w.bits, w.alpha, w.offset, w.x, w.g, rows=rows)
+        return rows.size
+
     with threadpool_limits(limits=1):
-        while rows_done < w.N and time.perf_counter() - t0 < budget_s:
-            rows = np.arange(rows_done, min(w.N, rows_done + block))
-            oracle.gemv(w.bits, w.alpha, w.offset, w.x, w.g, rows=rows)
-            rows_done += rows.size
+        if threads == 1:
+            rows_done = 0
+            for r0 in starts:
+                n = one(r0)
+                if n == 0:
+                    break
+                rows_done += n
+        else:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                rows_done = sum(ex.map(one, starts))
     el = time.perf_counter() - t0
-    full_s = el * w.N / rows_done
-    return full_s, rows_done, el
+    return el * w.N / max(rows_done, 1), rows_done, el
+
+
+def stream_peak(lg, torch, dev, nbytes=256 << 20, total=4 << 30, launches=400):
+    """Achievable HBM read rate of this GPU: the library's streaming-read kernel
+    over rotating buffers of nbytes (>= total bytes in all, so the last-level
+    cache cannot serve repeats), non-temporal loads, event pair over `launches`
+    launches after as many warm-up launches. Returns GB/s."""
+    R = max(1, -(-total // nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    for k in range(launches):
+        lg.stream_read(bufs[k % R].data_ptr(), nbytes, sink.data_ptr(), sink.numel(), True, sh)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(launches):
+        lg.stream_read(bufs[k % R].data_ptr(), nbytes, sink.data_ptr(), sink.numel(), True, sh)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / launches
+    del bufs
+    torch.cuda.empty_cache()
+    return nbytes / t / 1e9
 
 
 def load_workload(name):
@@ -94,16 +160,21 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=20000,
-                    help="untimed launches first (about a second: the clocks take that long to settle)")
+    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed launches before the warm-up, for at least this many seconds "
+                         "and one pass over the rotating copies (clocks and caches settle)")
     ap.add_argument("--workload", default="opt175b_ffn_up")
-    ap.add_argument("--kernel", choices=["lut", "dequant"], default="lut",
+    ap.add_argument("--kernel", choices=["lut", "dequant", "stream"], default="lut",
                     help="lut: the LUT-GEMV (the product); dequant: the dequantizing comparison "
-                         "kernel on the same packed data")
+                         "kernel on the same packed data; stream: the streaming-read kernel over "
+                         "buffers of the workload's algorithmic bytes (the achievable ceiling)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct weight copies cycled through (0: enough for >= 4 GiB, at "
                          "most 4096 copies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-peak", action="store_true",
+                    help="skip measuring the streaming-read ceiling after the timed region")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed region, copy MIB MiB device to device 5 times "
                          "(a known-size reference for HBM byte counters)")
@@ -137,6 +208,7 @@ def main():
         pw0 = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g, device=dev)
     has_off = pw0.has_offset
     nbytes = algorithmic_bytes(w.N, w.K, w.q, w.g, w.m, has_off)
+    nflops = algorithmic_flops(w.N, w.K, w.q, w.g, w.m, has_off)
     weight_bytes = pw0.d_bits.numel() + 2 * pw0.d_alpha.numel() + \
         (2 * pw0.d_offset.numel() if has_off else 0)
     # Enough distinct copies that no part of the weights can stay in the 256 MB
@@ -146,28 +218,40 @@ def main():
     # that at every group size here; tiny shapes, which are launch-bound, stop
     # at 4096 copies.
     R = args.rotate if args.rotate > 0 else min(4096, max(1, -(-(4 << 30) // weight_bytes)))
-    copies = [pw0]
-    for _ in range(R - 1):
-        copies.append(lg.PackedBCQ(w.N, w.K, w.q, w.g, pw0.d_bits.clone(), pw0.d_alpha.clone(),
-                                   pw0.d_offset.clone() if has_off else None))
     x = torch.from_numpy(w.x).to(dev)
     y = torch.empty((w.m, w.N), dtype=torch.float16, device=dev)
-    ws_bytes = lg.workspace_size(w.N, w.K, w.q, w.g, has_off, w.m)
-    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    args_c = [(c.shape, c.d_bits.data_ptr(), c.d_alpha.data_ptr(),
-               c.d_offset.data_ptr() if has_off else None) for c in copies]
+    if args.kernel == "stream":
+        # the same algorithmic bytes as one contiguous buffer per copy (16-byte multiple)
+        sbytes = -(-nbytes // 16) * 16
+        R = args.rotate if args.rotate > 0 else min(4096, max(1, -(-(4 << 30) // sbytes)))
+        del pw0
+        bufs = [torch.ones(sbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+        sink = torch.zeros(4096, dtype=torch.int32, device=dev)
 
-    if args.kernel == "lut":
         def launch(k):
-            shape, b, a, o = args_c[k % R]
-            lg.lutgemm_run(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(),
-                           ws.data_ptr() if ws_bytes else None, ws_bytes, sh)
+            lg.stream_read(bufs[k % R].data_ptr(), sbytes, sink.data_ptr(), sink.numel(), True, sh)
+        ws_bytes = 0
+        weight_bytes = sbytes
     else:
-        def launch(k):
-            shape, b, a, o = args_c[k % R]
-            lg.bcq_dequant_gemv(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(), sh)
+        copies = [pw0]
+        for _ in range(R - 1):
+            copies.append(lg.PackedBCQ(w.N, w.K, w.q, w.g, pw0.d_bits.clone(), pw0.d_alpha.clone(),
+                                       pw0.d_offset.clone() if has_off else None))
+        ws_bytes = lg.workspace_size(w.N, w.K, w.q, w.g, has_off, w.m)
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        args_c = [(c.shape, c.d_bits.data_ptr(), c.d_alpha.data_ptr(),
+                   c.d_offset.data_ptr() if has_off else None) for c in copies]
+        if args.kernel == "lut":
+            def launch(k):
+                shape, b, a, o = args_c[k % R]
+                lg.lutgemm_run(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(),
+                               ws.data_ptr() if ws_bytes else None, ws_bytes, sh)
+        else:
+            def launch(k):
+                shape, b, a, o = args_c[k % R]
+                lg.bcq_dequant_gemv(shape, w.m, b, a, o, x.data_ptr(), y.data_ptr(), sh)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -179,9 +263,20 @@ def main():
         log(f"copy calibration: 5 device copies of {n} bytes")
         del src, dst
     torch.cuda.synchronize()
-    log(f"{R} rotating weight copies ({R * weight_bytes / 2**30:.2f} GiB); warmup {args.warmup}")
+    log(f"{R} rotating copies ({R * weight_bytes / 2**30:.2f} GiB); settle >= {args.settle_s} s, "
+        f"then warmup {args.warmup}")
+    # settle: untimed launches in batches, for at least settle_s seconds of
+    # wall clock and at least one pass over all R copies
+    t_s = time.perf_counter()
+    n_settle = 0
+    while n_settle < R or time.perf_counter() - t_s < args.settle_s:
+        for _ in range(200):
+            launch(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_s
     for k in range(args.warmup):
-        launch(k)
+        launch(n_settle + k)
     torch.cuda.synchronize()
 
     # timed region: K back-to-back products between two synchronizations; a HIP
@@ -207,25 +302,56 @@ def main():
         launch(k)
         ends[k].record(stream)
     torch.cuda.synchronize()
-    durs_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    durs_us = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3
+    p10, p50, p90 = (float(np.percentile(durs_us, v)) for v in (10, 50, 90))
     log(f"timed {K_steps} steps in {t_total * 1e3:.2f} ms wall, {avg_kernel_s * 1e6:.2f} us per "
-        f"launch on the GPU clock; single-launch events: median {np.median(durs_ms) * 1e3:.2f} us, "
-        f"p10 {np.percentile(durs_ms, 10) * 1e3:.2f}, p90 {np.percentile(durs_ms, 90) * 1e3:.2f}")
+        f"launch on the GPU clock; single-launch events: p10 {p10:.2f} us, median {p50:.2f}, "
+        f"p90 {p90:.2f}")
 
     ms_per_step = t_total * 1e3 / K_steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / avg_kernel_s / 1e9
+    achieved_gbs = nbytes / avg_kernel_s / 1e9
+    achieved_tflops = nflops / avg_kernel_s / 1e12
+    hbm_frac = achieved_gbs / HBM_PEAK_GBS
+    alu_frac = achieved_tflops / ALU_PEAK_TFLOPS
+    # the bound is the larger of the two algorithmic floors
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_alu = nflops / (ALU_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_alu or args.kernel == "stream":
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_frac, 4)}
+    else:
+        roof = {"bound": "alu", "achieved": round(achieved_tflops, 3),
+                "peak": round(ALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s", "frac": round(alu_frac, 4)}
     # counters were taken with the default rotation (weights streamed from HBM)
-    traffic = stored_traffic(w.name) if args.kernel == "lut" and args.rotate == 0 else None
+    roof["traffic"] = (stored_traffic(w.name) if args.kernel == "lut" and args.rotate == 0
+                       else None)
+    roof["floor_us"] = {"hbm": round(t_hbm * 1e6, 3), "alu": round(t_alu * 1e6, 3)}
+    roof["hbm_frac"] = round(hbm_frac, 4)
+    roof["alu_frac"] = round(alu_frac, 4)
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = nflops
+
+    if not args.no_stream_peak and args.kernel != "stream":
+        peak_meas = stream_peak(lg, torch, dev)
+        roof["hbm_peak_measured"] = round(peak_meas, 1)
+        roof["hbm_frac_of_measured"] = round(achieved_gbs / peak_meas, 4)
+        log(f"streaming-read ceiling: {peak_meas:.1f} GB/s (256 MiB buffers over 4 GiB, "
+            f"non-temporal loads); this kernel {achieved_gbs:.1f} GB/s = "
+            f"{achieved_gbs / peak_meas:.3f} of it")
 
     cpu = None
     if not args.no_cpu_baseline:
-        full_s, rows, el = cpu_baseline(w)
-        cpu = {"value": round(nbytes / full_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+        cores = len(os.sched_getaffinity(0))
+        full_s, rows, el = cpu_baseline(w, cores, 12.0)
+        full1, rows1, el1 = cpu_baseline(w, 1, 8.0)
+        cpu = {"value": round(nbytes / full_s / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
-               "sample": (f"fp64 oracle (reconstruct W_hat rows, direct dot) on rows 0..{rows} of "
-                          f"{w.N} in {el:.1f}s with one BLAS thread, scaled to the full product: "
-                          f"{full_s:.1f} s/GEMV")}
+               "sample": (f"fp64 oracle (reconstruct W_hat rows, direct dot) on {rows} of {w.N} "
+                          f"rows in {el:.1f}s, {cores} threads each running it on its own "
+                          f"256-row blocks with one BLAS thread, scaled to the full product: "
+                          f"{full_s:.2f} s/GEMV; one thread: {rows1} rows in {el1:.1f}s, "
+                          f"{full1:.2f} s/GEMV ({nbytes / full1 / 1e9:.4f} GB/s)")}
         log(f"cpu baseline: {cpu['sample']}")
 
     out = {
@@ -236,10 +362,12 @@ def main():
         "n_gpus": 1,
         "steps": K_steps,
         "warmup": args.warmup,
+        "settle": {"launches": n_settle, "seconds": round(settle_s, 3)},
         "ms_per_step": round(ms_per_step, 5),
         "us_per_gemv": round(ms_per_step * 1e3, 2),
         "us_per_gemv_gpu_clock": round(avg_kernel_s * 1e6, 2),
-        "us_per_gemv_single_launch_median": round(float(np.median(durs_ms)) * 1e3, 2),
+        "us_per_gemv_single_launch": {"p10": round(p10, 2), "p50": round(p50, 2),
+                                      "p90": round(p90, 2)},
         "lookups_per_s": round(w.m * w.N * w.q * (w.K // 8) / avg_kernel_s, 0),
         "higher_is_better": True,
         "scaling": "weak",
@@ -249,10 +377,9 @@ def main():
         "config": {"workload": w.name, "kernel": args.kernel,
                    "N": w.N, "K": w.K, "q": w.q, "g": w.g, "m": w.m,
                    "offset": bool(has_off), "x": "fp16", "y": "fp16",
+                   "weights": f"{w.q} sign planes + fp16 scales per {w.g} inputs",
                    "rotating_copies": R, "algorithmic_bytes": nbytes},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -67,7 +67,9 @@ typedef enum lutgemm_status {
                                /* offset, or a rewritten scale that overflows fp16   */
   LUTGEMM_ERR_BUFFER = 4,      /* an output buffer or the workspace is too small     */
   LUTGEMM_ERR_ALIGN = 5,       /* a device pointer is not aligned as required        */
-  LUTGEMM_ERR_UNSUPPORTED = 6, /* the current device is not gfx950                   */
+  LUTGEMM_ERR_UNSUPPORTED = 6, /* the current device is not gfx950 (the environment  */
+                               /* variable LUTGEMM_FAKE_ARCH, a debugging aid,      */
+                               /* replaces the name the device reports)             */
   LUTGEMM_ERR_HIP = 7,         /* a HIP runtime call or a kernel launch failed       */
   LUTGEMM_ERR_INTERNAL = 8     /* unexpected internal failure                        */
 } lutgemm_status;
@@ -108,7 +110,13 @@ int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes);
  * captured in a graph). */
 int lutgemm_workspace_init(void* d_workspace, size_t bytes, void* stream);
 
-/* Pack a BCQ matrix from the logical format into the device format.
+/* Pack a BCQ matrix from the logical format into the device format. The
+ * logical format is the method's weight representation: q sign planes with
+ * one scale per (plane, row, group of g inputs) and an optional per-group
+ * offset (Elamur card "LUT-GEMM -- paper by Park et al. (2022)", sections
+ * "Summary" and "Interesting ideas: Group size as a separate
+ * hyper-parameter"; pith.science page of the same title, original abstract).
+ * The packed layout is this library's own (see the conventions above).
  * Host only (CPU), deterministic: the output bytes are fully determined by
  * the inputs. `offset` must be non-NULL exactly when s->has_offset.
  * Rejects non-finite alpha/offset values (LUTGEMM_ERR_VALUE) and output
@@ -137,12 +145,20 @@ int bcq_pack_uniform(const lutgemm_shape* s, const uint8_t* codes,
 
 /* y = W_hat x on the current HIP device, enqueued on `stream` (a hipStream_t;
  * NULL for the default stream). Asynchronous: returns after the launch.
+ * This is the LUT-GEMM product (Elamur card "LUT-GEMM -- paper by Park et al.
+ * (2022)", sections "Summary" and "Interesting ideas: Lookup tables instead
+ * of multiplications"; pith.science page of the same title, original
+ * abstract): fp16 activations times the BCQ weights, with the 256 signed sums
+ * of every 8-input chunk of x computed once per table and selected by each
+ * weight byte, so the weights are never expanded.
  *   d_bits, d_alpha, d_offset: packed device format (d_offset only when
  *       s->has_offset, else ignored);
  *   d_x  fp16 [m][K] row-major;  d_y  fp16 [m][N] row-major, overwritten;
  *   d_workspace: at least lutgemm_workspace_size bytes, zero-filled before its
  *       first use (may be NULL when that size is 0); calls that overlap in time
- *       must not share a workspace.
+ *       must not share a workspace. The size query assumes a full 256-CU
+ *       MI355X; on a device with another number of compute units the launch
+ *       chooses its own work split and limits it to workspace_bytes.
  * Alignment (else LUTGEMM_ERR_ALIGN): d_bits, d_x and d_workspace 16 bytes,
  * d_alpha and d_offset 4 bytes, d_y 2 bytes.
  * Arithmetic: table entries, scaling and accumulation in fp32; y rounded to
@@ -207,6 +223,21 @@ int bcq_quantize(const lutgemm_shape* s, const uint16_t* w, int32_t iters, uint8
 int bcq_dequant_gemv(const lutgemm_shape* s, int32_t m, const void* d_bits,
                      const void* d_alpha, const void* d_offset, const void* d_x,
                      void* d_y, void* stream);
+
+/* Measurement aid, not part of the method: read `bytes` of device memory at
+ * d_src once with 128-bit loads (one workgroup of 16 waves per compute unit,
+ * all workgroups reading one window of memory together, four loads in flight
+ * per thread), non-temporal when `nontemporal` is 1. This is the achievable
+ * HBM read rate the GEMV's bandwidth is compared against. The loaded values are
+ * folded and, almost never, written to d_sink (uint32, at least one entry per
+ * compute unit, sink_count entries). Alignment: d_src 16 bytes, d_sink 4.
+ * bytes < 4 GiB - 64 KiB (else LUTGEMM_ERR_SHAPE); reads past `bytes` inside
+ * the last 64 KiB block return zero without touching memory. Asynchronous on
+ * `stream`. Errors: LUTGEMM_ERR_NULL, LUTGEMM_ERR_ALIGN, LUTGEMM_ERR_VALUE
+ * (nontemporal not 0/1), LUTGEMM_ERR_BUFFER (sink_count too small),
+ * LUTGEMM_ERR_HIP. */
+int lutgemm_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, size_t sink_count,
+                        int nontemporal, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ __all__ = [
     "LIB_PATH", "LutGemmError", "Shape", "lib", "abi_version", "status_string",
     "check_shape", "packed_sizes", "workspace_size", "workspace_init",
     "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "footprint_bits",
-    "search_group_sizes", "bcq_quantize", "PackedBCQ", "STATUS",
+    "search_group_sizes", "bcq_quantize", "stream_read", "PackedBCQ", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
                                ctypes.POINTER(ctypes.c_double)]
     L.bcq_dequant_gemv.restype = ctypes.c_int
     L.bcq_dequant_gemv.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
+    L.lutgemm_stream_read.restype = ctypes.c_int
+    L.lutgemm_stream_read.argtypes = [_P, _SZ, _P, _SZ, ctypes.c_int, _P]
     _LIB = L
     return L
 
@@ -255,6 +257,13 @@ def bcq_dequant_gemv(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: 
                                   d_y, stream), "bcq_dequant_gemv")
 
 
+def stream_read(d_src: int, nbytes: int, d_sink: int, sink_count: int, nontemporal: bool,
+                stream: Optional[int]):
+    """Measurement aid: read ``nbytes`` of device memory once (lutgemm_stream_read)."""
+    _check(lib().lutgemm_stream_read(d_src, int(nbytes), d_sink, int(sink_count),
+                                     int(bool(nontemporal)), stream), "lutgemm_stream_read")
+
+
 class PackedBCQ:
     """A packed BCQ weight in device memory, ready for :meth:`__call__`.
 
@@ -267,7 +276,7 @@ class PackedBCQ:
         self.has_offset = d_offset is not None
         self.shape = _shape(N, K, q, g, self.has_offset)
         self.d_bits, self.d_alpha, self.d_offset = d_bits, d_alpha, d_offset
-        self._ws = None
+        self._ws = {}   # stream handle -> workspace tensor
 
     @classmethod
     def _upload(cls, N, K, q, g, pb, pa, po, device):
@@ -291,18 +300,30 @@ class PackedBCQ:
         obj.n_rounded = n_r
         return obj
 
-    def workspace(self, m: int):
-        """A zero-filled device workspace large enough for batch m (kept and reused;
-        each completed call leaves its counters zero)."""
+    def workspace(self, m: int, stream=None):
+        """A zero-filled device workspace large enough for batch m on ``stream``
+        (default: the current stream), or ``(None, 0)`` when none is needed.
+
+        Calls that overlap in time must not share a workspace, so one is kept per
+        stream and reused by every later call on that stream (each completed call
+        leaves its counters zero). It is allocated while that stream is current,
+        so when a larger one replaces it the allocator reuses the old memory only
+        in that stream's order."""
         import torch
         need = workspace_size(self.N, self.K, self.q, self.g, self.has_offset, m)
         if need == 0:
             return None, 0
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.d_bits.device)
-            workspace_init(self._ws.data_ptr(), need,
-                           torch.cuda.current_stream(self._ws.device).cuda_stream)
-        return self._ws, self._ws.numel()
+        dev = self.d_bits.device
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        key = stream.cuda_stream
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < need:
+            with torch.cuda.stream(stream):
+                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace_init(ws.data_ptr(), need, key)
+            self._ws[key] = ws
+        return ws, ws.numel()
 
     def _check_io(self, x, out):
         import torch
@@ -322,8 +343,9 @@ class PackedBCQ:
         m = x.shape[0]
         if out is None:
             out = torch.empty((m, self.N), dtype=torch.float16, device=x.device)
-        ws, ws_bytes = self.workspace(m)
-        stream = torch.cuda.current_stream(x.device).cuda_stream
+        strm = torch.cuda.current_stream(x.device)
+        ws, ws_bytes = self.workspace(m, strm)
+        stream = strm.cuda_stream
         lutgemm_run(self.shape, m, self.d_bits.data_ptr(), self.d_alpha.data_ptr(),
                     self.d_offset.data_ptr() if self.d_offset is not None else None,
                     x.data_ptr(), out.data_ptr(),

@@ -69,7 +69,7 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     try:
         objs = [os.path.join(tmp, "pack.o"), os.path.join(tmp, "lutgemv.o"),
                 os.path.join(tmp, "dequant.o"), os.path.join(tmp, "footprint.o"),
-                os.path.join(tmp, "quantize.o")]
+                os.path.join(tmp, "quantize.o"), os.path.join(tmp, "probe.o")]
         jobs = [
             [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "pack.cpp"), "-o", objs[0]],
             [CXX, *CXX_FLAGS, *incs, "-c", os.path.join(CSRC, "footprint.cpp"), "-o", objs[3]],
@@ -78,6 +78,8 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
              os.path.join(CSRC, "lutgemv.hip"), "-o", objs[1]],
             [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c", "-Rpass-analysis=kernel-resource-usage",
              os.path.join(CSRC, "dequant.hip"), "-o", objs[2]],
+            [HIPCC, *HIP_FLAGS, *extra_hip_flags, *incs, "-c",
+             os.path.join(CSRC, "probe.hip"), "-o", objs[5]],
         ]
         # the kernel instances of each plane count q build in their own unit
         for q in range(1, 9):

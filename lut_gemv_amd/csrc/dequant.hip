@@ -22,7 +22,10 @@
 //    SIMD) rather than by an explicit prefetch ring.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "layout.h"
 #include "lutgemm.h"
@@ -43,6 +46,25 @@ struct DqParams {
 };
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+std::atomic<int> g_dq_arch[64];   // 0 unknown, 1 gfx950, 2 other
+
+// The current device must be gfx950 (LUTGEMM_FAKE_ARCH, a debugging aid,
+// replaces the reported name and bypasses the per-device cache).
+int dq_check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LUTGEMM_ERR_HIP;
+  const char* fake = getenv("LUTGEMM_FAKE_ARCH");
+  const bool use_cache = dev >= 0 && dev < 64 && !(fake && *fake);
+  int known = use_cache ? g_dq_arch[dev].load(std::memory_order_relaxed) : 0;
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LUTGEMM_ERR_HIP;
+    known = strncmp((fake && *fake) ? fake : prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (use_cache) g_dq_arch[dev].store(known, std::memory_order_relaxed);
+  }
+  return known == 1 ? LUTGEMM_OK : LUTGEMM_ERR_UNSUPPORTED;
+}
 
 __device__ __forceinline__ uint32_t bcast_half(uint32_t word, int hi) {
   // (h, h) from half `hi` of word
@@ -227,11 +249,8 @@ extern "C" int bcq_dequant_gemv(const lutgemm_shape* s, int32_t m, const void* d
         (G.has_offset && !dq_aligned(d_offset, 4)))
       return LUTGEMM_ERR_ALIGN;
   }
-  int dev = 0;
-  hipDeviceProp_t prop;
-  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-    return LUTGEMM_ERR_HIP;
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return LUTGEMM_ERR_UNSUPPORTED;
+  st = dq_check_device();
+  if (st) return st;
   if (G.K == 0) {
     const size_t n = (size_t)m * G.N;
     const size_t want = (n + 255) / 256;

@@ -62,6 +62,12 @@ struct Config {
   size_t ws_bytes;
 };
 
+// Workspace of a launch whose input dimension is split S ways: the arrival
+// counters, then fp32 partial sums [S][m][Npad].
+size_t split_ws_bytes(const Geometry& G, int64_t m, int64_t S) {
+  return kCounterBytes + (size_t)S * (size_t)m * (size_t)G.Npad * sizeof(float);
+}
+
 struct TileOverride {
   int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1, pr = -1, ei = -1;
 };
@@ -81,8 +87,9 @@ bool tile_override(TileOverride* o) {
 
 // Pick waves, rows per wave, batch rows per item, row tiles per item, the
 // split of the input tiles and the ring depth. The kernel is persistent (one
-// workgroup per CU, LDS-bound), so each CU works through ceil(items / kCUs)
-// items.
+// workgroup per CU, LDS-bound), so each of the `cus` compute units works
+// through ceil(items / cus) items. Splits whose workspace would exceed
+// `max_ws` bytes are not considered (no split needs none).
 //
 // Batch 1 with grouped scales (the HBM-bound case): when the matrix has
 // between 8 and 16 row tiles per CU, each CU takes one row block of
@@ -97,7 +104,7 @@ bool tile_override(TileOverride* o) {
 // tiles it covers and its batch rows (a tile step of 16 row tiles is one unit;
 // 8-wave instances pay for their lower latency hiding), plus a small cost per
 // item and one for the split reduction.
-Config choose_config(const Geometry& G, int64_t m) {
+Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws) {
   Config c{};
   c.gq = (G.g % 32) == 0;
   c.W = 0;   // stays 0 if no instance fits (reported as an internal error)
@@ -110,7 +117,7 @@ Config choose_config(const Geometry& G, int64_t m) {
   const bool off = G.has_offset;
   // batch 1 with x small enough: stage it in LDS (16-wave instances)
   const bool xl_ok = m == 1 && G.KT * kChunkTile <= kXChunks;
-  const int64_t ri1 = (G.RT + kCUs - 1) / kCUs;
+  const int64_t ri1 = (G.RT + cus - 1) / cus;
   // x in LDS with the 2-deep ring, else the 3-deep ring with x from L2
   const bool xl1 = xl_ok && pick_kernel(q, 1, 1, true, off, 16, 0, true) != nullptr;
   const KernelFn deep = pick_kernel(q, 1, 1, true, off, 16, 3, false);
@@ -151,8 +158,9 @@ Config choose_config(const Geometry& G, int64_t m) {
       const int64_t n_bg = (m + v.mc - 1) / v.mc;
       const int64_t smax = G.KT < 64 ? G.KT : 64;
       for (int64_t s = 1; s <= smax; ++s) {
+        if (s > 1 && split_ws_bytes(G, m, s) > max_ws) break;
         const int64_t items = n_rb * n_bg * s;
-        const int64_t per_cu = (items + kCUs - 1) / kCUs;
+        const int64_t per_cu = (items + cus - 1) / cus;
         const int64_t tiles = (G.KT + s - 1) / s;
         const double unit = v.eff * (double)rows * v.mc / 16.0;
         const double step = unit + v.bar * v.mc;
@@ -200,6 +208,7 @@ Config choose_config(const Geometry& G, int64_t m) {
     if (o.s >= 1) c.S = (int)(o.s < G.KT ? o.s : (G.KT > 0 ? G.KT : 1));
   }
   if (c.S < 1) c.S = 1;
+  if (c.S > 1 && split_ws_bytes(G, m, c.S) > max_ws) c.S = 1;
   if (c.n_rb * c.n_bg > kMaxCounters) c.S = 1;   // counters live in a fixed region
   // batch 1 without x in LDS: each sign byte is still read once per product
   // (where a read-once instance exists for the choice, it differs from the
@@ -207,22 +216,36 @@ Config choose_config(const Geometry& G, int64_t m) {
   c.once = m == 1 && !c.xl && !c.pr && c.MC == 1 &&
            pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, c.ring, false, false, false, true) !=
                pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, c.ring, false, false, false, false);
-  c.ws_bytes = c.S > 1 ? kCounterBytes + (size_t)c.S * (size_t)m * (size_t)G.Npad * sizeof(float) : 0;
+  c.ws_bytes = c.S > 1 ? split_ws_bytes(G, m, c.S) : 0;
   return c;
 }
 
 std::atomic<int> g_arch_ok[64];   // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[64];       // compute units of the device, 0 unknown
 
-int check_device() {
+// The current device must be gfx950. LUTGEMM_FAKE_ARCH, a debugging aid,
+// replaces the name the device reports (so the refusal path can be exercised
+// on the real part); it is read on every call and bypasses the cache.
+int check_device(int* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LUTGEMM_ERR_HIP;
-  int known = (dev >= 0 && dev < 64) ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
-  if (known == 0) {
+  const bool cached = dev >= 0 && dev < 64;
+  const char* fake = getenv("LUTGEMM_FAKE_ARCH");
+  int known = (cached && !(fake && *fake)) ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
+  int n = cached ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (known == 0 || n <= 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LUTGEMM_ERR_HIP;
-    known = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    if (dev >= 0 && dev < 64) g_arch_ok[dev].store(known, std::memory_order_relaxed);
+    const char* name = (fake && *fake) ? fake : prop.gcnArchName;
+    known = strncmp(name, "gfx950", 6) == 0 ? 1 : 2;
+    n = prop.multiProcessorCount;
+    if (n <= 0) return LUTGEMM_ERR_HIP;
+    if (cached && !(fake && *fake)) {
+      g_arch_ok[dev].store(known, std::memory_order_relaxed);
+      g_cus[dev].store(n, std::memory_order_relaxed);
+    }
   }
+  *cus = n;
   return known == 1 ? LUTGEMM_OK : LUTGEMM_ERR_UNSUPPORTED;
 }
 
@@ -234,6 +257,91 @@ bool buffers_fit(const Geometry& G, int64_t m) {
   const uint64_t lim = 0xFFFFFFFFull;
   return G.bits_bytes <= lim && G.alpha_count * 2 <= lim && G.offset_count * 2 <= lim &&
          (uint64_t)m * (uint64_t)G.K * 2 <= lim;
+}
+
+// Enqueue the product for a validated shape and configuration (K > 0): the
+// kernel instance, its parameters and its persistent grid of min(items, cus)
+// workgroups. `ws` is the workspace of a split launch (counters, then partials).
+int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d_bits,
+           const void* d_alpha, const void* d_offset, const void* d_x, void* d_y, void* ws,
+           hipStream_t strm) {
+  KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr,
+                            c.ei, c.once);
+  if (!fn) return LUTGEMM_ERR_INTERNAL;
+  Params p{};
+  p.bits = (const uint8_t*)d_bits;
+  p.alpha = (const uint32_t*)d_alpha;
+  p.offset = G.has_offset ? (const uint32_t*)d_offset : nullptr;
+  p.x = (const uint16_t*)d_x;
+  p.y = (uint16_t*)d_y;
+  p.counters = c.S > 1 ? (uint32_t*)ws : nullptr;
+  p.partial = c.S > 1 ? (float*)((char*)ws + kCounterBytes) : nullptr;
+  p.N = (int)G.N;
+  p.K = (int)G.K;
+  p.g = (int)G.g;
+  p.m = (int)m;
+  p.C = (int)G.C;
+  p.KT = (int)G.KT;
+  p.RT = (int)G.RT;
+  p.G = (int)G.G;
+  p.S = c.S;
+  p.Npad = (int)G.Npad;
+  p.n_rb = (int)c.n_rb;
+  p.ri = c.RI;
+  p.g_shift = -1;
+  for (int b = 3; b < 31; ++b)
+    if (((int64_t)1 << b) == G.g) p.g_shift = b;
+  p.g_span = (int)((kChunkTile * 8 + G.g - 1) / G.g + 1);
+  p.g_tile = (kChunkTile * 8) % G.g == 0 ? 1 : 0;
+  p.n_bg = (int)c.n_bg;
+  // Batch groups of one weight block side by side on one XCD (see decode_item):
+  // measured 0.7-1.8 us faster at 2 and 3 batch groups of one-row items; at 4
+  // it moved by -0.8..+0.3 us from one machine to another, and with paired tables at 4..16
+  // groups it was slower (each round then streams few distinct blocks).
+  p.xcd_bg = (!c.pr && c.n_bg > 1 && c.n_bg <= 3 && (c.n_rb * c.S) % 8 == 0) ? 1 : 0;
+  const int64_t items = c.n_rb * c.n_bg * c.S;
+  if (items > 0x7FFFFFFF - (int64_t)cus) return LUTGEMM_ERR_SHAPE;
+  p.n_items = (int)items;
+  dim3 grid((unsigned)(items < cus ? items : cus));
+  void* args[] = {&p};
+  if (hipLaunchKernel((const void*)fn, grid, dim3(64 * c.W), args, 0, strm) != hipSuccess)
+    return LUTGEMM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
+}
+
+// y = 0 for an empty reduction (K = 0).
+int launch_zero_y(void* d_y, size_t n, hipStream_t strm) {
+  const size_t want = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, strm, (uint16_t*)d_y, n);
+  return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
+}
+
+// Checks shared by the entry points that run a product: shape, batch, buffer
+// limits and the pointers and alignments of the operands (not the workspace).
+// Returns LUTGEMM_OK with *nothing = 1 when there is no output to write.
+int check_operands(const lutgemm_shape* s, int32_t m, const void* d_bits, const void* d_alpha,
+                   const void* d_offset, const void* d_x, const void* d_y, Geometry* G,
+                   int* nothing) {
+  *nothing = 0;
+  int st = check_shape(s);
+  if (st) return st;
+  if (m < 0 || m > kMaxBatch) return LUTGEMM_ERR_SHAPE;
+  *G = geometry(s);
+  if (!buffers_fit(*G, m)) return LUTGEMM_ERR_SHAPE;
+  if (m == 0 || G->N == 0) {
+    *nothing = 1;
+    return LUTGEMM_OK;
+  }
+  if (!d_y) return LUTGEMM_ERR_NULL;
+  if (!aligned(d_y, 2)) return LUTGEMM_ERR_ALIGN;
+  if (G->K > 0) {
+    if (!d_bits || !d_alpha || !d_x || (G->has_offset && !d_offset)) return LUTGEMM_ERR_NULL;
+    if (!aligned(d_bits, 16) || !aligned(d_x, 16) || !aligned(d_alpha, 4) ||
+        (G->has_offset && !aligned(d_offset, 4)))
+      return LUTGEMM_ERR_ALIGN;
+  }
+  return LUTGEMM_OK;
 }
 
 }  // namespace
@@ -252,7 +360,7 @@ int lutgemm_workspace_size(const lutgemm_shape* s, int32_t m, size_t* bytes) {
   *bytes = 0;
   if (!buffers_fit(G, m)) return LUTGEMM_ERR_SHAPE;
   if (m == 0 || G.N == 0 || G.K == 0) return LUTGEMM_OK;
-  const Config c = choose_config(G, m);
+  const Config c = choose_config(G, m, kNominalCUs, SIZE_MAX);
   if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
   *bytes = c.ws_bytes;
   return LUTGEMM_OK;
@@ -272,21 +380,14 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
                 const void* d_offset, const void* d_x, void* d_y, void* d_workspace,
                 size_t workspace_bytes, void* stream) {
   try {
-    int st = check_shape(s);
-    if (st) return st;
-    if (m < 0 || m > kMaxBatch) return LUTGEMM_ERR_SHAPE;
-    Geometry G = geometry(s);
-    if (!buffers_fit(G, m)) return LUTGEMM_ERR_SHAPE;
-    if (m == 0 || G.N == 0) return LUTGEMM_OK;
-    if (!d_y) return LUTGEMM_ERR_NULL;
-    if (!aligned(d_y, 2)) return LUTGEMM_ERR_ALIGN;
+    Geometry G{};
+    int nothing = 0;
+    int st = check_operands(s, m, d_bits, d_alpha, d_offset, d_x, d_y, &G, &nothing);
+    if (st || nothing) return st;
+    // the workspace the size query promised for this shape (a full 256-CU part)
     Config c{};
     if (G.K > 0) {
-      if (!d_bits || !d_alpha || !d_x || (G.has_offset && !d_offset)) return LUTGEMM_ERR_NULL;
-      if (!aligned(d_bits, 16) || !aligned(d_x, 16) || !aligned(d_alpha, 4) ||
-          (G.has_offset && !aligned(d_offset, 4)))
-        return LUTGEMM_ERR_ALIGN;
-      c = choose_config(G, m);
+      c = choose_config(G, m, kNominalCUs, SIZE_MAX);
       if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
       if (c.ws_bytes) {
         if (!d_workspace) return LUTGEMM_ERR_NULL;
@@ -294,60 +395,18 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
         if (!aligned(d_workspace, 16)) return LUTGEMM_ERR_ALIGN;
       }
     }
-    st = check_device();
+    int cus = 0;
+    st = check_device(&cus);
     if (st) return st;
     hipStream_t strm = (hipStream_t)stream;
-
-    if (G.K == 0) {  // empty reduction: y = 0
-      const size_t n = (size_t)m * G.N;
-      const size_t want = (n + 255) / 256;
-      const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
-      hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, strm, (uint16_t*)d_y, n);
-      return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
+    if (G.K == 0) return launch_zero_y(d_y, (size_t)m * G.N, strm);
+    // a device with another number of compute units gets its own choice, with
+    // its split limited to the workspace passed
+    if (cus != kNominalCUs) {
+      c = choose_config(G, m, cus, d_workspace ? workspace_bytes : 0);
+      if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
     }
-
-    KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr,
-                              c.ei, c.once);
-    if (!fn) return LUTGEMM_ERR_INTERNAL;
-    Params p{};
-    p.bits = (const uint8_t*)d_bits;
-    p.alpha = (const uint32_t*)d_alpha;
-    p.offset = G.has_offset ? (const uint32_t*)d_offset : nullptr;
-    p.x = (const uint16_t*)d_x;
-    p.y = (uint16_t*)d_y;
-    p.counters = c.S > 1 ? (uint32_t*)d_workspace : nullptr;
-    p.partial = c.S > 1 ? (float*)((char*)d_workspace + kCounterBytes) : nullptr;
-    p.N = (int)G.N;
-    p.K = (int)G.K;
-    p.g = (int)G.g;
-    p.m = m;
-    p.C = (int)G.C;
-    p.KT = (int)G.KT;
-    p.RT = (int)G.RT;
-    p.G = (int)G.G;
-    p.S = c.S;
-    p.Npad = (int)G.Npad;
-    p.n_rb = (int)c.n_rb;
-    p.ri = c.RI;
-    p.g_shift = -1;
-    for (int b = 3; b < 31; ++b)
-      if (((int64_t)1 << b) == G.g) p.g_shift = b;
-    p.g_span = (int)((kChunkTile * 8 + G.g - 1) / G.g + 1);
-    p.g_tile = (kChunkTile * 8) % G.g == 0 ? 1 : 0;
-    p.n_bg = (int)c.n_bg;
-    // Batch groups of one weight block side by side on one XCD (see decode_item):
-    // measured 0.7-1.8 us faster at 2 and 3 batch groups of one-row items; at 4
-    // it moved by -0.8..+0.3 us from one machine to another, and with paired tables at 4..16
-    // groups it was slower (each round then streams few distinct blocks).
-    p.xcd_bg = (!c.pr && c.n_bg > 1 && c.n_bg <= 3 && (c.n_rb * c.S) % 8 == 0) ? 1 : 0;
-    const int64_t items = c.n_rb * c.n_bg * c.S;
-    if (items > 0x7FFFFFFF - kCUs) return LUTGEMM_ERR_SHAPE;
-    p.n_items = (int)items;
-    dim3 grid((unsigned)(items < kCUs ? items : kCUs));
-    void* args[] = {&p};
-    if (hipLaunchKernel((const void*)fn, grid, dim3(64 * c.W), args, 0, strm) != hipSuccess)
-      return LUTGEMM_ERR_HIP;
-    return hipGetLastError() == hipSuccess ? LUTGEMM_OK : LUTGEMM_ERR_HIP;
+    return launch(G, m, c, cus, d_bits, d_alpha, d_offset, d_x, d_y, d_workspace, strm);
   } catch (...) {
     return LUTGEMM_ERR_INTERNAL;
   }

@@ -58,7 +58,9 @@ constexpr int kLutWords = 256 * kChunkTile;   // one table tile: 64 KiB of fp32 
 // At batch 1 the whole of x can be staged in LDS next to the two tables (128 KiB):
 // up to 1920 chunks of 8 inputs (30 KiB), i.e. K <= 15360.
 constexpr int kXChunks = 1920;
-constexpr int kCUs = 256;                     // MI355X compute units (dispatch heuristic)
+// Compute units of a full MI355X. The workspace size query (host only) sizes the
+// split reduction for this count; launches use the device's own count.
+constexpr int kNominalCUs = 256;
 // Split reductions keep their arrival counters in a fixed region at the start
 // of the workspace, so any later call finds its counters zero whatever its shape.
 constexpr size_t kCounterBytes = 64 * 1024;

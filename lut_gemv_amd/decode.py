@@ -172,13 +172,17 @@ class DecodeStack:
         return self.outs[self.out_name]
 
     def capture(self, kernel: str = "lut"):
-        """Capture one token into a HIP graph (after an eager token, which sets up
-        any split-K workspaces outside the capture)."""
+        """Capture one token into a HIP graph. An eager token runs first on the
+        capture stream, so the split-K workspaces (one per stream) are set up
+        outside the capture and the graph reuses them."""
         import torch
-        self.token(kernel)
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            self.token(kernel)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=cs):
             self.token(kernel)
         torch.cuda.synchronize()
         self.graph, self.graph_kernel = g, kernel
@@ -226,10 +230,13 @@ class DecodeStack:
                 else:
                     w.dequant(src, out=self.outs[name])
 
-        run()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            run()                                # workspaces of the capture stream
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=cs):
             run()
         for _ in range(warmup):
             g.replay()

@@ -70,13 +70,14 @@ def test_tiny_all_outputs():
     _check(_gpu_y(pw, w.x), w)
 
 
-def test_opt175b_ffn_up_sampled():
+def test_opt175b_ffn_up_all_outputs():
+    """The benchmark's workload in the launch configuration it times, every output."""
     w = workloads.generate("opt175b_ffn_up")
     _say("opt175b_ffn_up 49152x12288 q3 g128 m1")
     pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
     y = _gpu_y(pw, w.x)
     assert np.isfinite(y).all()
-    _check(y, w, rows=_sample_rows(w.N, 2048))
+    _check(y, w)
 
 
 def test_opt175b_ffn_up_shard_all_outputs():
@@ -126,12 +127,12 @@ def test_llama7b_int4_uniform_all_outputs():
 
 
 @pytest.mark.parametrize("m", [4, 16, 32])
-def test_decode_batch_sampled(m):
+def test_decode_batch_all_outputs(m):
     w = workloads.generate(f"decode_m{m}")
     _say(f"decode m={m} 12288x12288 q3 g128")
     pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
     y = _gpu_y(pw, w.x)
-    _check(y, w, rows=_sample_rows(w.N, 512, seed=m))
+    _check(y, w)
 
 
 @pytest.mark.parametrize("q", [1, 2, 4])
@@ -309,16 +310,26 @@ def test_xcd_grouped_batch_groups_all_outputs(monkeypatch, tile, N, K, m):
 
 
 def test_workspace_reuse_across_shapes():
-    """One workspace serves a large split call, then a smaller one, then the large again."""
+    """One workspace (through the C ABI) serves a large split call, then a smaller
+    one, then the large again: each completed call leaves its counters zero."""
     big = workloads.random_bcq(8192, 12288, 3, 128, m=1, seed=6)
     small = workloads.random_bcq(1024, 4096, 2, 64, m=3, seed=7)
     pb = lg.PackedBCQ.from_bcq(big.bits, big.alpha, None, big.g)
     ps = lg.PackedBCQ.from_bcq(small.bits, small.alpha, None, small.g)
-    ps._ws = pb.workspace(1)[0]        # share
+    nb = lg.workspace_size(big.N, big.K, big.q, big.g, False, 1)
+    ns = lg.workspace_size(small.N, small.K, small.q, small.g, False, 3)
+    assert nb > 0 and ns > 0
+    ws = torch.empty(max(nb, ns), dtype=torch.uint8, device=DEV)
+    sh = torch.cuda.current_stream().cuda_stream
+    lg.workspace_init(ws.data_ptr(), ws.numel(), sh)
     _say("workspace reuse")
     for w, p in [(big, pb), (small, ps), (big, pb), (small, ps)]:
-        y = _gpu_y(p, w.x)
-        _check(y, w, rows=_sample_rows(w.N, 256))
+        x = torch.from_numpy(w.x).to(DEV)
+        y = torch.empty((w.m, w.N), dtype=torch.float16, device=DEV)
+        lg.lutgemm_run(p.shape, w.m, p.d_bits.data_ptr(), p.d_alpha.data_ptr(), None,
+                       x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), sh)
+        torch.cuda.synchronize()
+        _check(y.cpu().numpy(), w, rows=_sample_rows(w.N, 256))
 
 
 def test_large_batch_and_many_rows():
@@ -347,3 +358,132 @@ def test_quantized_fp16_matrix_end_to_end():
     pw = lg.PackedBCQ.from_bcq(bits, alpha, None, g)
     w = workloads.Workload("quantized", N, K, q, g, m, x, bits, alpha, None)
     _check(_gpu_y(pw, x), w)
+
+
+def test_cancelling_planes_with_activation_outliers():
+    """Planes that cancel plus activation outliers: in every chunk the first input
+    is 1000 and its two plane bits are opposite with equal scales, so its weight
+    is exactly 0; the outlier then enters both table entries of a row but not the
+    bound sum_k |W_hat x|. fp16 table entries fail this input (the worst output
+    at about 11x the tolerance, in an exact simulation of such entries); the fp32
+    tables must pass it on every output."""
+    rng = np.random.default_rng(31)
+    N, K, q, g = 256, 4096, 2, 128
+    x = rng.standard_normal((1, K))
+    x[0, ::8] = 1000.0
+    x = x.astype(np.float16)
+    bits = rng.integers(0, 256, size=(q, N, K // 8), dtype=np.uint8)
+    bits[1] = bits[0] ^ 0x01                      # bit 0 (input 8c) opposite in the two planes
+    a0 = (np.abs(rng.standard_normal((N, K // g))) * 0.02).astype(np.float16)
+    alpha = np.stack([a0, a0])                    # equal scales: the outlier's weight is 0
+    w = workloads.Workload("cancel_outlier", N, K, q, g, 1, x, bits, alpha, None)
+    Wh = oracle.reconstruct_rows(bits, alpha, None, g, np.arange(N))
+    assert (Wh[:, ::8] == 0).all()
+    _say("cancelling planes + outliers")
+    pw = lg.PackedBCQ.from_bcq(bits, alpha, None, g)
+    _check(_gpu_y(pw, x), w)
+
+
+@pytest.mark.parametrize("kind", ["nan", "inf"])
+def test_non_finite_x_propagates(kind):
+    """x is not checked: a NaN or an infinity in x makes every output non-finite,
+    as in the exact product (every row reads every input). The kind may differ:
+    an infinite input can give NaN where the exact product is infinite, because
+    the table entries are built as differences (IEEE inf - inf)."""
+    w = workloads.random_bcq(500, 2048, 3, 128, m=2, seed=41, with_offset=True)
+    x = w.x.copy()
+    x[0, 777] = np.float16(np.nan) if kind == "nan" else np.float16(np.inf)
+    x[1, 5] = np.float16(np.nan) if kind == "nan" else -np.float16(np.inf)
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    _say(f"non-finite x ({kind})")
+    y = _gpu_y(pw, x).astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref, _ = oracle.gemv(w.bits, w.alpha, w.offset, x, w.g)
+    assert (~np.isfinite(ref)).all()
+    assert (~np.isfinite(y)).all()
+    if kind == "nan":
+        assert np.isnan(y).all()
+
+
+def test_maximum_split_all_outputs(monkeypatch):
+    """The input dimension split 64 ways (the most the dispatcher uses) on a shape
+    with 16 row blocks and 4 items per workgroup: 1024 partial-sum items meet in
+    the fused reduction. Three runs, each checked on every output and bitwise
+    equal to the first; the loop stops at its first failure."""
+    w = workloads.random_bcq(4096, 32768, 3, 128, m=1, seed=43, name="split64_4096x32768")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    ref = oracle.gemv(w.bits, w.alpha, None, w.x, w.g)
+    x = torch.from_numpy(w.x).to(DEV)
+    monkeypatch.setenv("LUTGEMM_TILE", "1,64,16,1")
+    first = None
+    for rep in range(3):
+        _say(f"split 64, run {rep}")
+        y = pw(x)
+        torch.cuda.synchronize()
+        yn = y.cpu().numpy()
+        _check(yn, w, ref=ref)
+        if first is None:
+            first = yn
+        else:
+            assert np.array_equal(yn.view(np.uint16), first.view(np.uint16))
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
+def test_two_streams_share_a_weight():
+    """Split launches of one weight on two streams at once: each stream has its
+    own workspace, and both results match the oracle."""
+    w = workloads.random_bcq(6144, 12288, 3, 128, m=1, seed=44)
+    assert lg.workspace_size(w.N, w.K, w.q, w.g, False, 1) > 0
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    x = torch.from_numpy(w.x).to(DEV)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    _say("two streams")
+    ys = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            ys.append(pw(x))
+        with torch.cuda.stream(s2):
+            ys.append(pw(x))
+    torch.cuda.synchronize()
+    assert len(pw._ws) >= 2
+    ref = oracle.gemv(w.bits, w.alpha, None, w.x, w.g)
+    for y in ys:
+        _check(y.cpu().numpy(), w, ref=ref)
+
+
+def test_fake_arch_is_refused_before_launch(monkeypatch):
+    """LUTGEMM_FAKE_ARCH makes the device report another architecture: both
+    products refuse with LUTGEMM_ERR_UNSUPPORTED and write nothing."""
+    w = workloads.random_bcq(64, 512, 2, 128, m=1, seed=45)
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    x = torch.from_numpy(w.x).to(DEV)
+    y = torch.full((1, 64), 3.0, dtype=torch.float16, device=DEV)
+    monkeypatch.setenv("LUTGEMM_FAKE_ARCH", "gfx942")
+    _say("fake arch")
+    with pytest.raises(lg.LutGemmError) as e:
+        pw(x, out=y)
+    assert e.value.status == 6
+    with pytest.raises(lg.LutGemmError) as e:
+        pw.dequant(x, out=y)
+    assert e.value.status == 6
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+    monkeypatch.delenv("LUTGEMM_FAKE_ARCH")
+    _check(_gpu_y(pw, w.x), w)
+
+
+def test_stream_read_probe_runs():
+    """The streaming-read measurement kernel reads a buffer and writes nothing
+    (its fold equals the magic value only by a 2^-32 chance per workgroup)."""
+    n = (64 << 20) + 4096
+    src = torch.ones(n, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(1024, dtype=torch.int32, device=DEV)
+    sh = torch.cuda.current_stream().cuda_stream
+    lg.stream_read(src.data_ptr(), n, sink.data_ptr(), sink.numel(), True, sh)
+    lg.stream_read(src.data_ptr(), n, sink.data_ptr(), sink.numel(), False, sh)
+    torch.cuda.synchronize()
+    assert (sink == 0).all()
+    with pytest.raises(lg.LutGemmError):
+        lg.stream_read(src.data_ptr() + 8, n - 16, sink.data_ptr(), sink.numel(), True, sh)

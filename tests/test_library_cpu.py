@@ -443,3 +443,52 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stderr)
     assert r.stdout.strip() == lg.status_string(2)
+
+
+def test_stream_read_validates_before_any_hip_call():
+    """The streaming-read measurement kernel reports argument errors without the GPU."""
+    L = lg.lib()
+    A = 0x100000
+    assert L.lutgemm_stream_read(A, 0, A, 1, 1, None) == 0           # nothing to read
+    assert L.lutgemm_stream_read(None, 64, A, 1, 1, None) == 1
+    assert L.lutgemm_stream_read(A, 64, None, 1, 1, None) == 1
+    assert L.lutgemm_stream_read(A + 8, 64, A, 1, 1, None) == 5
+    assert L.lutgemm_stream_read(A, 64, A + 2, 1, 1, None) == 5
+    assert L.lutgemm_stream_read(A, 64, A, 1, 2, None) == 3
+    assert L.lutgemm_stream_read(A, 64, A, 0, 1, None) == 4
+    assert L.lutgemm_stream_read(A, 1 << 32, A, 1, 1, None) == 2
+
+
+def test_packed_workspace_is_kept_per_stream(monkeypatch):
+    """PackedBCQ keeps one workspace per stream (calls that overlap in time must
+    not share one): the same stream gets the same buffer back, another stream its
+    own, and a larger need replaces only that stream's buffer. CPU tensors and
+    stand-in streams; no GPU."""
+    import contextlib
+
+    import torch
+
+    class FakeStream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+    sizes = {1: 1000, 4: 3000}
+    inits = []
+    monkeypatch.setattr(lg, "workspace_size", lambda N, K, q, g, off, m: sizes.get(m, 0))
+    monkeypatch.setattr(lg, "workspace_init", lambda p, n, s: inits.append((n, s)))
+    monkeypatch.setattr(torch.cuda, "stream", lambda s: contextlib.nullcontext())
+    pw = lg.PackedBCQ(64, 512, 3, 128, torch.zeros(16, dtype=torch.uint8),
+                      torch.zeros(16, dtype=torch.int16))
+    s1, s2 = FakeStream(11), FakeStream(22)
+    a, na = pw.workspace(1, s1)
+    b, nb = pw.workspace(1, s1)
+    c, nc = pw.workspace(1, s2)
+    assert a is b and na == nb == 1000
+    assert c is not a and nc == 1000
+    assert inits == [(1000, 11), (1000, 22)]
+    d, nd = pw.workspace(4, s1)                    # grows on s1 only
+    assert nd == 3000 and d is not a
+    assert pw.workspace(1, s2)[0] is c
+    assert pw.workspace(1, s1)[0] is d            # a larger buffer serves smaller needs
+    assert inits[-1] == (3000, 11)
+    assert pw.workspace(2, s1) == (None, 0)       # no split: no workspace
