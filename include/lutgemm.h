@@ -175,6 +175,32 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits,
                 void* d_y, void* d_workspace, size_t workspace_bytes,
                 void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product as lutgemm_run, with the same operands, alignment rules, status codes
+ * and asynchrony, but no workspace argument and no allocation of any kind.
+ * Where the input dimension is split across workgroups, the arrival counters
+ * and fp32 partial sums live in a fixed scratch array inside the library, one
+ * per GPU, held until the process ends; its size is
+ * lutgemm_noalloc_scratch_bytes() (4 MiB). The launch is chosen among those
+ * whose partial sums fit that scratch (a smaller split, down to none, when the
+ * best one would not), so every valid shape runs; a split forced through the
+ * LUTGEMM_TILE tuning override that would not fit is refused with
+ * LUTGEMM_ERR_BUFFER before any HIP call. The first call on a device clears
+ * the scratch's counters with a kernel on `stream`; every completed call leaves
+ * them zero. All calls on one GPU share its scratch, so calls that overlap in
+ * time on one GPU (on different streams, or from different threads) race and
+ * must be ordered by the caller. Results can differ in rounding from
+ * lutgemm_run's when the two choose different splits, and stay within the
+ * same tolerance. */
+int lutgemm_run_noalloc(const lutgemm_shape* s, int32_t m, const void* d_bits,
+                        const void* d_alpha, const void* d_offset, const void* d_x,
+                        void* d_y, void* stream);
+
+/* Size in bytes of the scratch array lutgemm_run_noalloc uses on each GPU.
+ * Never fails; host only. */
+size_t lutgemm_noalloc_scratch_bytes(void);
+
 /* Storage in bits of the matrix of shape *s: q sign bits per weight, one fp16
  * scale per (plane, row, group of g) and one fp16 offset per (row, group) when
  * s->has_offset (Elamur card, section "Interesting ideas: Group size as a

@@ -21,7 +21,8 @@ __all__ = [
     "LIB_PATH", "LutGemmError", "Shape", "lib", "abi_version", "status_string",
     "check_shape", "packed_sizes", "workspace_size", "workspace_init",
     "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "footprint_bits",
-    "search_group_sizes", "bcq_quantize", "stream_read", "PackedBCQ", "STATUS",
+    "search_group_sizes", "bcq_quantize", "stream_read", "lutgemm_run_noalloc",
+    "noalloc_scratch_bytes", "PackedBCQ", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +98,10 @@ def lib() -> ctypes.CDLL:
                                ctypes.POINTER(ctypes.c_double)]
     L.bcq_dequant_gemv.restype = ctypes.c_int
     L.bcq_dequant_gemv.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
+    L.lutgemm_run_noalloc.restype = ctypes.c_int
+    L.lutgemm_run_noalloc.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
+    L.lutgemm_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    L.lutgemm_noalloc_scratch_bytes.argtypes = []
     L.lutgemm_stream_read.restype = ctypes.c_int
     L.lutgemm_stream_read.argtypes = [_P, _SZ, _P, _SZ, ctypes.c_int, _P]
     _LIB = L
@@ -216,6 +221,19 @@ def lutgemm_run(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: Optio
     """Raw entry point: device addresses as integers, ``stream`` a hipStream_t handle."""
     _check(lib().lutgemm_run(ctypes.byref(shape), int(m), d_bits, d_alpha, d_offset, d_x, d_y,
                              d_workspace, int(workspace_bytes), stream), "lutgemm_run")
+
+
+def lutgemm_run_noalloc(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offset: Optional[int],
+                        d_x: int, d_y: int, stream: Optional[int]):
+    """Raw entry point that allocates nothing (its split partials live in the
+    library's per-GPU scratch); calls that overlap in time on one GPU race."""
+    _check(lib().lutgemm_run_noalloc(ctypes.byref(shape), int(m), d_bits, d_alpha, d_offset, d_x,
+                                     d_y, stream), "lutgemm_run_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the per-GPU scratch array of :func:`lutgemm_run_noalloc`."""
+    return lib().lutgemm_noalloc_scratch_bytes()
 
 
 def footprint_bits(N: int, K: int, q: int, g: int, has_offset: bool = False) -> int:

@@ -8,12 +8,23 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "layout.h"
 #include "lutgemm.h"
 #include "lutgemv_kernel.h"
 
 namespace lutgemm {
+
+// ------------------------------------------------------------------ scratch
+// Device memory of lutgemm_run_noalloc: the split reduction's arrival counters
+// (first kCounterBytes) and fp32 partial sums, in a file-scope array that every
+// GPU the library runs on holds until the process ends. In host code the name
+// `scratch` is only a stand-in: its device address is fetched per device with
+// hipGetSymbolAddress and only that address is used.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 __global__ void zero_fill_kernel(uint16_t* y, size_t n) {
@@ -259,6 +270,43 @@ bool buffers_fit(const Geometry& G, int64_t m) {
          (uint64_t)m * (uint64_t)G.K * 2 <= lim;
 }
 
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[64];     // device address of `scratch`, per device
+std::atomic<int> g_scratch_zeroed[64];    // counters cleared on a stream not being captured
+
+// The device address of this device's scratch, fetched once per device (with
+// that device current); the first call also clears the arrival counters with
+// a kernel on `strm`, so this call's launch, which follows on the same stream,
+// finds them zero. A clear recorded into a graph being captured does not count:
+// the next call outside a capture clears them again.
+int device_scratch(int dev, hipStream_t strm, void** out) {
+  if (dev < 0 || dev >= 64) return LUTGEMM_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr || !g_scratch_zeroed[dev].load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LUTGEMM_ERR_HIP;
+      ptr = p;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    if (!g_scratch_zeroed[dev].load(std::memory_order_relaxed)) {
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(strm, &cap) != hipSuccess) {
+        (void)hipGetLastError();               // unknown: clear again next time
+        cap = hipStreamCaptureStatusActive;
+      }
+      hipLaunchKernelGGL(zero_bytes_kernel, dim3((unsigned)(kCounterBytes / 256)), dim3(256), 0,
+                         strm, (uint8_t*)ptr, kCounterBytes);
+      if (hipGetLastError() != hipSuccess) return LUTGEMM_ERR_HIP;
+      if (cap == hipStreamCaptureStatusNone) g_scratch_zeroed[dev].store(1, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return LUTGEMM_OK;
+}
+
 // Enqueue the product for a validated shape and configuration (K > 0): the
 // kernel instance, its parameters and its persistent grid of min(items, cus)
 // workgroups. `ws` is the workspace of a split launch (counters, then partials).
@@ -411,5 +459,44 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
     return LUTGEMM_ERR_INTERNAL;
   }
 }
+
+int lutgemm_run_noalloc(const lutgemm_shape* s, int32_t m, const void* d_bits,
+                        const void* d_alpha, const void* d_offset, const void* d_x, void* d_y,
+                        void* stream) {
+  try {
+    Geometry G{};
+    int nothing = 0;
+    int st = check_operands(s, m, d_bits, d_alpha, d_offset, d_x, d_y, &G, &nothing);
+    if (st || nothing) return st;
+    // a split forced by the tuning override is refused, not changed, when its
+    // workspace would not fit the scratch
+    if (G.K > 0) {
+      const Config forced = choose_config(G, m, kNominalCUs, SIZE_MAX);
+      if (forced.W == 0) return LUTGEMM_ERR_INTERNAL;
+      TileOverride o;
+      if (tile_override(&o) && o.s > 1 && forced.ws_bytes > kScratchBytes) return LUTGEMM_ERR_BUFFER;
+    }
+    int cus = 0;
+    st = check_device(&cus);
+    if (st) return st;
+    hipStream_t strm = (hipStream_t)stream;
+    if (G.K == 0) return launch_zero_y(d_y, (size_t)m * G.N, strm);
+    const Config c = choose_config(G, m, cus, kScratchBytes);
+    if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
+    if (c.ws_bytes > kScratchBytes) return LUTGEMM_ERR_BUFFER;
+    void* ws = nullptr;
+    if (c.ws_bytes) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return LUTGEMM_ERR_HIP;
+      st = device_scratch(dev, strm, &ws);
+      if (st) return st;
+    }
+    return launch(G, m, c, cus, d_bits, d_alpha, d_offset, d_x, d_y, ws, strm);
+  } catch (...) {
+    return LUTGEMM_ERR_INTERNAL;
+  }
+}
+
+size_t lutgemm_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 }  // extern "C"

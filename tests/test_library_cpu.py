@@ -492,3 +492,30 @@ def test_packed_workspace_is_kept_per_stream(monkeypatch):
     assert pw.workspace(1, s1)[0] is d            # a larger buffer serves smaller needs
     assert inits[-1] == (3000, 11)
     assert pw.workspace(2, s1) == (None, 0)       # no split: no workspace
+
+
+def test_run_noalloc_validates_before_any_hip_call(monkeypatch):
+    """lutgemm_run_noalloc reports argument errors, and refuses a forced split
+    whose partial sums would not fit its scratch, without touching the GPU."""
+    L = lg.lib()
+    assert L.lutgemm_noalloc_scratch_bytes() == 4 << 20
+    ok = lg.Shape(64, 512, 3, 128, 0)
+    A = 0x100000
+
+    def run(shape, m, b=A, a=A, o=None, x=A, y=A):
+        return L.lutgemm_run_noalloc(ctypes.byref(shape) if shape is not None else None, m, b, a,
+                                     o, x, y, None)
+    assert run(None, 1) == 1
+    assert run(lg.Shape(64, 12, 3, 128, 0), 1) == 2
+    assert run(ok, -1) == 2 and run(ok, 65536) == 2
+    assert run(ok, 0) == 0 and run(lg.Shape(0, 512, 3, 128, 0), 1) == 0
+    assert run(ok, 1, y=None) == 1 and run(ok, 1, b=None) == 1
+    assert run(lg.Shape(64, 512, 3, 128, 1), 1, o=None) == 1
+    assert run(ok, 1, b=A + 8) == 5 and run(ok, 1, x=A + 2) == 5
+    # 64 splits x 8 batch rows x 4096 rows x 4 bytes = 8 MiB of partial sums
+    big = lg.Shape(4096, 32768, 3, 128, 0)
+    monkeypatch.setenv("LUTGEMM_TILE", "1,64,16,1")
+    assert run(big, 8) == 4
+    monkeypatch.setenv("LUTGEMM_TILE", "1,8,16,1")      # 1 MiB: fits, so it reaches the device check
+    assert run(big, 8) == 7
+    monkeypatch.delenv("LUTGEMM_TILE")
