@@ -60,6 +60,23 @@ KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring,
   }
 }
 
+// The nibble-table unit kernel for q planes: upw units per wave, ring depth nr
+// (0: the deepest built for upw), or nullptr.
+KernelFn pick_nibble(int q, bool off, int upw, int nr) {
+  switch (q) {
+    case 1: return nibble_kernel_of_q<1>(off, upw, nr);
+    case 2: return nibble_kernel_of_q<2>(off, upw, nr);
+    case 3: return nibble_kernel_of_q<3>(off, upw, nr);
+    case 4: return nibble_kernel_of_q<4>(off, upw, nr);
+    case 5: return nibble_kernel_of_q<5>(off, upw, nr);
+    case 6: return nibble_kernel_of_q<6>(off, upw, nr);
+    case 7: return nibble_kernel_of_q<7>(off, upw, nr);
+    case 8: return nibble_kernel_of_q<8>(off, upw, nr);
+    default: return nullptr;
+  }
+}
+
+
 struct Config {
   int RPW, MC, S, W;
   int RI;                // row tiles per row block (<= W * RPW)
@@ -68,6 +85,8 @@ struct Config {
   bool pr;               // paired tables (two batch rows per table entry)
   bool ei;               // early-issue ring (x in LDS, two register sets)
   bool once;             // batch 1 without x in LDS: non-temporal sign-plane loads
+  bool us;               // the nibble-table unit kernel (batch 1, few row tiles per CU)
+  int upw, nr;           // its units per wave and ring depth
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
@@ -80,19 +99,23 @@ size_t split_ws_bytes(const Geometry& G, int64_t m, int64_t S) {
 }
 
 struct TileOverride {
-  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1, pr = -1, ei = -1;
+  int rpw = 0, s = 0, w = 0, mc = 0, ring = 0, ri = 0, xl = -1, pr = -1, ei = -1, us = -1;
 };
 
-// Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR[,EI]]]]]]]" (LUTGEMM_TILE);
+// Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR[,EI[,US]]]]]]]]" (LUTGEMM_TILE);
 // never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
 // (default: where possible). PR: 1 paired tables where an instance has them, 0
 // never (default: the dispatcher's choice). EI: 1 the early-issue ring where
-// x is staged in LDS with the default ring, 0 never (the default).
+// x is staged in LDS with the default ring, 0 never (the default). US: 1 the
+// nibble-table unit kernel where it applies (batch 1, scale groups dividing or
+// multiples of 512 inputs, x in LDS) with RI row tiles per workgroup (default:
+// ceil(row tiles / CUs)) and ring depth `ring` (0: its default), 0 never, -1
+// the dispatcher's choice. With US = 1 the other fields are ignored.
 bool tile_override(TileOverride* o) {
   const char* e = getenv("LUTGEMM_TILE");
   if (!e || !*e) return false;
-  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc, &o->ring,
-                       &o->ri, &o->xl, &o->pr, &o->ei);
+  const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc,
+                       &o->ring, &o->ri, &o->xl, &o->pr, &o->ei, &o->us);
   return n >= 2;
 }
 
@@ -115,7 +138,8 @@ bool tile_override(TileOverride* o) {
 // tiles it covers and its batch rows (a tile step of 16 row tiles is one unit;
 // 8-wave instances pay for their lower latency hiding), plus a small cost per
 // item and one for the split reduction.
-Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws) {
+Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
+                     bool allow_units = true) {
   Config c{};
   c.gq = (G.g % 32) == 0;
   c.W = 0;   // stays 0 if no instance fits (reported as an internal error)
@@ -133,7 +157,32 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws) {
   const bool xl1 = xl_ok && pick_kernel(q, 1, 1, true, off, 16, 0, true) != nullptr;
   const KernelFn deep = pick_kernel(q, 1, 1, true, off, 16, 3, false);
   const bool has_deep = deep && deep != pick_kernel(q, 1, 1, true, off, 16, 0, false);
-  if (m == 1 && c.gq && ri1 >= 8 && ri1 <= 16 && (xl1 || has_deep)) {
+  // The nibble-table unit kernel: batch 1, scale groups that divide an input
+  // tile or are whole input tiles, x in LDS, and a workgroup of ri1 row tiles
+  // with at most 8 (row tile, plane) units (half its waves) over at most 16
+  // input tiles (one phase of tables). Measured against the split launch on 14
+  // shapes (4096..28672 rows, 512..12288 inputs, q = 1..4): it won or tied
+  // on every shape inside these bounds and lost by 5-70% on every shape
+  // outside them (more units or a second phase), where the 4-input lookups
+  // (two reads and four address operations per weight byte) cost more than
+  // the table builds they save.
+  const int upw1 = (int)((ri1 * q + 15) / 16);
+  const bool us_g = c.gq && (512 % G.g == 0 || G.g % 512 == 0);
+  const bool us1 = allow_units && m == 1 && us_g && xl_ok && ri1 * q <= 8 &&
+                   G.KT <= kPhaseTiles && pick_nibble(q, off, upw1, 0) != nullptr;
+  if (us1) {
+    c.us = true;
+    c.W = 16;
+    c.RPW = 1;
+    c.MC = 1;
+    c.RI = (int)ri1;
+    c.upw = upw1;
+    c.nr = 0;
+    c.xl = true;
+    c.n_rb = (G.RT + ri1 - 1) / ri1;
+    c.n_bg = 1;
+    c.S = 1;
+  } else if (m == 1 && c.gq && ri1 >= 8 && ri1 <= 16 && (xl1 || has_deep)) {
     c.W = 16;
     c.RPW = 1;
     c.MC = 1;
@@ -195,7 +244,31 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws) {
     c.xl = !c.pr && xl_ok && pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, 0, true) != nullptr;
   }
   TileOverride o;
-  if (tile_override(&o)) {
+  const bool have_o = tile_override(&o);
+  // the unit kernel declined: the choice without it (which applies the
+  // override's other fields itself)
+  if (have_o && o.us == 0 && c.us) return choose_config(G, m, cus, max_ws, false);
+  if (have_o && o.us == 1) {
+    const int64_t ri = (o.ri >= 1 && o.ri <= 64) ? o.ri : ri1;
+    const int upw = (int)((ri * q + 15) / 16);
+    if (m == 1 && us_g && xl_ok && pick_nibble(q, off, upw, o.ring)) {
+      c = Config{};
+      c.gq = true;
+      c.us = true;
+      c.W = 16;
+      c.RPW = 1;
+      c.MC = 1;
+      c.RI = (int)ri;
+      c.upw = upw;
+      c.nr = o.ring;
+      c.xl = true;
+      c.n_rb = (G.RT + ri - 1) / ri;
+      c.n_bg = 1;
+      c.S = 1;
+      c.ws_bytes = 0;
+      return c;
+    }
+  } else if (have_o) {
     const int w = o.w ? o.w : c.W;
     const int mc = o.mc ? o.mc : c.MC;
     const bool pr = o.pr > 0;
@@ -205,6 +278,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws) {
     const bool ei = o.ei > 0 && xl && o.ring < 3 &&
                     pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, xl, pr, true) != nullptr;
     if (pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, xl, pr)) {
+      c.us = false;
       c.W = w;
       c.RPW = o.rpw;
       c.MC = mc;
@@ -313,8 +387,9 @@ int device_scratch(int dev, hipStream_t strm, void** out) {
 int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d_bits,
            const void* d_alpha, const void* d_offset, const void* d_x, void* d_y, void* ws,
            hipStream_t strm) {
-  KernelFn fn = pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl, c.pr,
-                            c.ei, c.once);
+  KernelFn fn = c.us ? pick_nibble((int)G.q, G.has_offset, c.upw, c.nr)
+                     : pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl,
+                                   c.pr, c.ei, c.once);
   if (!fn) return LUTGEMM_ERR_INTERNAL;
   Params p{};
   p.bits = (const uint8_t*)d_bits;
@@ -350,7 +425,8 @@ int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d
   const int64_t items = c.n_rb * c.n_bg * c.S;
   if (items > 0x7FFFFFFF - (int64_t)cus) return LUTGEMM_ERR_SHAPE;
   p.n_items = (int)items;
-  dim3 grid((unsigned)(items < cus ? items : cus));
+  // the unit kernel runs one item per workgroup; the others are persistent
+  dim3 grid((unsigned)(c.us ? items : (items < cus ? items : cus)));
   void* args[] = {&p};
   if (hipLaunchKernel((const void*)fn, grid, dim3(64 * c.W), args, 0, strm) != hipSuccess)
     return LUTGEMM_ERR_HIP;

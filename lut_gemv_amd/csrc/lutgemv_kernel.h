@@ -560,33 +560,59 @@ __device__ __forceinline__ void lookups_pair(const LaneCtx& l, int h, const floa
   }
 }
 
+// Sum each of a lane's four row accumulators (rows 4*r4 + a) over the 16
+// lanes that share its row quad (lanes differing in bits 0-2 and 5), with
+// cross-lane moves that do not go through LDS: v_permlane32_swap exchanges the
+// two halves of the wave (rows 0 and 1 stay in lanes 0-31, rows 2 and 3 go to
+// lanes 32-63), then three DPP moves within rows of 16 lanes: a quad swap that
+// leaves row 2*bit5 + bit0 in each lane, a quad swap over bit 1 and a shift by
+// 4 over bit 2. The result is the sum of row reduced_row(lane) in the lanes with
+// (lane & 6) == 4 (partial sums elsewhere). The order of the additions is fixed.
+__device__ __forceinline__ float row_sum16(const float (&v)[4], int lane) {
+  float w[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v[k]),
+                                                    __builtin_bit_cast(unsigned, v[k + 2]), false,
+                                                    false);
+    w[k] = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+  const bool odd = (lane & 1) != 0;
+  const float keep = odd ? w[1] : w[0];
+  const float send = odd ? w[0] : w[1];
+  // quad_perm [1,0,3,2] (0xB1), quad_perm [2,3,0,1] (0x4E), row_shr:4 (0x114)
+  float t = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                                 __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+  t += __builtin_bit_cast(float,
+                          __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x4E, 0xF, 0xF, false));
+  t += __builtin_bit_cast(float,
+                          __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x114, 0xF, 0xF, false));
+  return t;
+}
+
+// The row (within its row tile) whose sum row_sum16 leaves in `lane`, and
+// whether that lane holds it.
+__device__ __forceinline__ int reduced_row(int lane) {
+  return 4 * ((lane >> 3) & 3) + ((lane & 32) ? 2 : 0) + (lane & 1);
+}
+__device__ __forceinline__ bool holds_row_sum(int lane) { return (lane & 6) == 4; }
+
 // Reduce the accumulators of a finished item over the 16 lanes that share a
-// row quad (lanes differing in bits 0-2 and 5), store them (fp16 y, or this
-// split's fp32 partials) and clear them. Each exchange halves the rows a lane
-// keeps; a lane ends with row 4*r4 + 2*bit5 + bit2 of its lane index. The
-// summation order is fixed.
+// row quad (row_sum16), store them (fp16 y, or this split's fp32 partials)
+// and clear them.
 template <int RPW, int MC>
 __device__ __forceinline__ void finish_item(const Params& p, const LaneCtx& l, const ItemCtx& c,
                                             float (&acc)[MC][RPW][4]) {
   const bool split_mode = p.S > 1;
-  const bool up32 = (l.lane & 32) != 0, up4 = (l.lane & 4) != 0;
 #pragma unroll
   for (int r = 0; r < MC; ++r) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       if (r < c.rows_here && i < c.valid_rpw) {
-        float v[4] = {acc[r][i][0], acc[r][i][1], acc[r][i][2], acc[r][i][3]};
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float lo = v[k], hi = v[k + 2];
-          v[k] = (up32 ? hi : lo) + __shfl_xor(up32 ? lo : hi, 32, 64);
-        }
-        const float lo = v[0], hi = v[1];
-        float t = (up4 ? hi : lo) + __shfl_xor(up4 ? lo : hi, 4, 64);
-        t += __shfl_xor(t, 2, 64);
-        t += __shfl_xor(t, 1, 64);
-        const int row = (c.rt_first + i) * kRowTile + 4 * l.r4 + (up32 ? 2 : 0) + (up4 ? 1 : 0);
-        if ((l.lane & 3) == 0) {
+        const float v[4] = {acc[r][i][0], acc[r][i][1], acc[r][i][2], acc[r][i][3]};
+        const float t = row_sum16(v, l.lane);
+        const int row = (c.rt_first + i) * kRowTile + reduced_row(l.lane);
+        if (holds_row_sum(l.lane)) {
           if (split_mode) {
             // device-scope store: written through to where every XCD reads it
             __hip_atomic_store(&p.partial[((size_t)c.split * p.m + (c.r0 + r)) * p.Npad + row], t,
@@ -854,6 +880,298 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
 }
 
+// ------------------------------------------------------------------ unit kernel
+// Batch 1 with few row tiles per compute unit (the nibble-table kernel below).
+// A workgroup takes ri row tiles over the whole input dimension, and the work
+// is spread over its 16 waves in units of one (row tile, plane): unit u = row
+// tile u / Q, plane u % Q of the workgroup, held by wave u % 16 (UPW units per
+// wave at most). Each wave keeps the loads of its units for the next NR input
+// tiles in flight. At the end each unit's 16 row sums are written to LDS and
+// added over the planes in plane order. No split of the input dimension: no
+// partial sums in memory.
+template <int UPW>
+struct UnitRegs {
+  uint4 bw[UPW];          // lane block of the unit's plane block
+  uint32_t aw[UPW][2];    // scales of the lane's four rows (fp16 pairs)
+  uint32_t ow[UPW][2];    // offsets of the lane's four rows (plane-0 units only)
+};
+
+// Where this wave's units are, computed once per workgroup (all uniform over the
+// wave but the lane offsets of the scales). The unit kernels take group sizes
+// that divide 512 (every input tile starts a group; a lane's group within the
+// tile is fixed) or are multiples of 512 (an input tile lies in one group).
+template <int Q, int UPW>
+struct UnitPlan {
+  bool on[UPW];            // unit exists in this workgroup
+  bool q0[UPW];            // unit holds plane 0 (adds the offset term)
+  uint32_t bits0[UPW];     // byte offset of the unit's block in input tile 0
+  uint32_t arow[UPW];      // the unit's row tile times the groups per row
+  uint32_t avoff[UPW];     // lane's byte offset in a scale block (per lane)
+  uint32_t ovoff;          // lane's byte offset in an offset block (per lane)
+  uint32_t tile_stride;    // bytes of packed sign planes per input tile
+  uint32_t ginc, gper;     // groups per input tile (g divides 512) / input tiles per group
+};
+
+template <int Q, int UPW>
+__device__ __forceinline__ UnitPlan<Q, UPW> unit_plan(const Params& p, const LaneCtx& l, int rt0,
+                                                    int nunits) {
+  UnitPlan<Q, UPW> P;
+  const bool tile_groups = (512 % p.g) == 0;
+  P.ginc = tile_groups ? (uint32_t)(512 / p.g) : 0u;
+  P.gper = tile_groups ? 0x7FFFFFFFu : (uint32_t)(p.g / 512);
+  const uint32_t g_rel = tile_groups ? (uint32_t)((32 * l.c4) >> p.g_shift) : 0u;
+  P.tile_stride = (uint32_t)p.RT * (uint32_t)(Q * 1024);
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int u = l.wave + 16 * j;
+    const int rtl = u / Q, q = u - (u / Q) * Q;
+    P.on[j] = u < nunits;
+    P.q0[j] = q == 0;
+    // blocks of consecutive row tiles are consecutive, plane by plane
+    P.bits0[j] = ((uint32_t)rt0 * Q + (uint32_t)u) * 1024u;
+    P.arow[j] = (uint32_t)(rt0 + rtl) * (uint32_t)p.G;
+    P.avoff[j] = g_rel * 32u * Q + (uint32_t)q * 32u + 8u * (uint32_t)l.r4;
+  }
+  P.ovoff = g_rel * 32u + 8u * (uint32_t)l.r4;
+  return P;
+}
+
+// The input tile whose loads are issued next: its index, its sign-plane offset
+// and its first scale group, advanced by a few scalar adds per tile.
+struct UnitCursor {
+  int kt;
+  uint32_t bts;            // kt * tile_stride
+  uint32_t grp, cnt;       // first group of the tile; tiles into that group
+};
+
+template <int Q, int UPW>
+__device__ __forceinline__ void advance(const UnitPlan<Q, UPW>& P, UnitCursor& c) {
+  c.kt += 1;
+  c.bts += P.tile_stride;
+  c.grp += P.ginc;
+  c.cnt += 1;
+  if (c.cnt == P.gper) {
+    c.cnt = 0;
+    c.grp += 1;
+  }
+}
+
+// Issue the loads of the cursor's tile for this wave's units (unconditional; a
+// unit past the workgroup's units or a tile past the end gets empty ranges),
+// then advance the cursor.
+template <int Q, bool OFF, int UPW>
+__device__ __forceinline__ void load_units(const Params& p, const LaneCtx& l,
+                                           const UnitPlan<Q, UPW>& P, UnitCursor& c,
+                                           UnitRegs<UPW>& R) {
+  const bool live = c.kt < p.KT;
+  // groups this tile's loads may touch (g_span, fewer at the end of a row)
+  const uint32_t span = (uint32_t)min(p.G - (int)c.grp, p.g_span);
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const bool on = live && P.on[j];
+    const uint32_t bs = P.bits0[j] + c.bts;
+    R.bw[j] = load16<true>(make_rsrc(p.bits, on ? bs + 1024u : 0u), l.block, bs);
+    const uint32_t blk = P.arow[j] + c.grp;
+    const uint32_t ab = blk * (32u * Q);
+    const uint2 a = load8(make_rsrc(p.alpha, on ? ab + span * (32u * Q) : 0u), P.avoff[j], ab);
+    R.aw[j][0] = a.x;
+    R.aw[j][1] = a.y;
+    if constexpr (OFF) {
+      const bool ono = on && P.q0[j];
+      const uint2 o = load8(make_rsrc(p.offset, ono ? (blk + span) * 32u : 0u), P.ovoff,
+                            blk * 32u);
+      R.ow[j][0] = o.x;
+      R.ow[j][1] = o.y;
+    }
+  }
+  advance(P, c);
+}
+
+// ------------------------------------------------------------------ nibble tables
+// The unit kernel with 4-input tables. Chunk t (8 inputs) is split into two
+// halves j (inputs 8t + 4j .. +3); the table of a half holds its 16 signed sums,
+// entry e = sum_s (bit s of e ? +x : -x). A weight byte b then selects
+// T[0][b & 15] + T[1][b >> 4], which is the 8-input table's entry b, so the
+// packed format is unchanged. The tables of 1024 chunks (8192 inputs, one
+// phase) take 128 KiB: entry e of half j of chunk t at word (2 e + j) * 1024 + t,
+// so the lanes of a lookup read consecutive chunks (no bank conflicts), and a
+// lane's base address and the tile's offset stay below 16 KiB (the tile's
+// offset goes in the read's immediate offset). They
+// are built once per phase (two phases at most, as x is staged whole), so the
+// loop over the input tiles has no table builds and no barriers: each wave
+// streams its units freely. A lookup costs two VALU operations for its address
+// (a rotate that brings the nibble to bits 13-16 and a mask-or with the
+// table's base) where the 8-input table needs one, and two reads per weight
+// byte instead of one; for workgroups with few row tiles the build it saves
+// costs more than that.
+constexpr int kPhaseChunks = 1024;                         // 8192 inputs per phase
+constexpr int kPhaseTiles = kPhaseChunks / kChunkTile;     // 16 input tiles
+
+// Tables of the phase that starts at chunk c0 (chunk c0 + t at column t): thread
+// t builds both halves of its chunk, 16 entries each, in Gray-code order.
+__device__ __forceinline__ void build_nibbles(float* lut, const uint4* xs, int c0, int nchunks) {
+  const int t = threadIdx.x;                    // 1024 threads = kPhaseChunks
+  if (c0 + t >= nchunks) return;
+  float x[8];
+  unpack8(xs[c0 + t], x);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float* h = x + 4 * j;
+    float T = -((h[0] + h[1]) + (h[2] + h[3]));  // entry 0: every sign negative
+    float two[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) two[b] = h[b] + h[b];
+    float* base = lut + j * kPhaseChunks + t;
+    base[0] = T;
+#pragma unroll
+    for (int n = 1; n < 16; ++n) {
+      const int b = __builtin_ctz(n);
+      const int e = n ^ (n >> 1);
+      T += ((e >> b) & 1) ? two[b] : -two[b];
+      base[2 * e * kPhaseChunks] = T;
+    }
+  }
+}
+
+template <int Q, bool OFF, int UPW, int NR>
+__global__ void __launch_bounds__(1024, 4) __attribute__((amdgpu_waves_per_eu(4, 4)))
+    lutgemv_nibble_kernel(Params p) {
+  static_assert(kPhaseTiles % NR == 0, "the ring depth divides the tiles of a phase");
+  __shared__ float lut[2 * 16 * kPhaseChunks];
+  __shared__ uint4 xs[kXChunks];
+  LaneCtx l = lane_ctx();
+  const int item = blockIdx.x;
+  const int rt0 = item * p.ri;
+  const int ri = min(p.ri, p.RT - rt0);
+  const int nunits = ri * Q;
+  const int nchunks = p.KT * kChunkTile;
+
+  constexpr int NX = (kXChunks + 1023) / 1024;
+  uint4 xr[NX];
+  {
+    const auto xrs = make_rsrc(p.x, (uint32_t)p.K * 2u);
+#pragma unroll
+    for (int j = 0; j < NX; ++j)
+      xr[j] = load16(xrs, ((uint32_t)threadIdx.x + (uint32_t)(j * 1024)) * 16u);
+    asm volatile("" ::: "memory");
+  }
+  const UnitPlan<Q, UPW> P = unit_plan<Q, UPW>(p, l, rt0, nunits);
+  const bool has_units = P.on[0];               // uniform over the wave
+  UnitCursor ic{0, 0u, 0u, 0u};                 // the tile whose loads go out next
+  UnitRegs<UPW> R[NR];
+  if (has_units) {
+#pragma unroll
+    for (int s = 0; s < NR; ++s) load_units<Q, OFF, UPW>(p, l, P, ic, R[s]);
+  }
+#pragma unroll
+  for (int j = 0; j < NX; ++j) {
+    const int c = (int)threadIdx.x + j * 1024;
+    if (c < nchunks) xs[c] = xr[j];
+  }
+  __syncthreads();
+  build_nibbles(lut, xs, 0, nchunks);
+  __syncthreads();
+
+  // per visit k and half j: the rotation that brings the half's nibble of byte
+  // b_k to bits 13-16, and the table base (half, chunk 4*c4 + b_k of the tile)
+  uint32_t rot[4][2], nbase[4][2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b = (uint32_t)((k + l.r4) & 3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      rot[k][j] = (8u * b + 4u * (uint32_t)j + 19u) & 31u;     // right by 8b + 4j - 13
+      nbase[k][j] = ((uint32_t)j << 12) | ((4u * (uint32_t)l.c4 + b) << 2);
+    }
+  }
+
+  float acc[UPW][4];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) acc[j][a] = 0.f;
+
+  // Steps leave the loop only after a whole phase, and every step issues its
+  // loads (empty past the end): the wait counts are the same on every path.
+  // Waves without units only take part in the builds.
+  for (int kt0 = 0; kt0 < p.KT; kt0 += kPhaseTiles) {
+    if (kt0 > 0) {                              // uniform: the next phase's tables
+      __syncthreads();
+      build_nibbles(lut, xs, kt0 * kChunkTile, nchunks);
+      __syncthreads();
+    }
+    if (!has_units) continue;
+#pragma unroll
+    for (int s = 0; s < kPhaseTiles; ++s) {
+      const int kt = kt0 + s;
+      UnitRegs<UPW>& cur = R[s % NR];
+      if (kt < p.KT) {                          // uniform over the workgroup
+        const uint32_t toff = (uint32_t)s * (kChunkTile * 4);   // the tile's chunks in the phase
+        float csum = 0.f;
+        if constexpr (OFF) {
+          bool has0 = false;
+#pragma unroll
+          for (int j = 0; j < UPW; ++j) has0 = has0 || (P.on[j] && P.q0[j]);
+          if (has0) {                            // entry 15 of both halves: the chunk's sum
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) csum += lut_at(lut, (nbase[k][j] | (15u << 13)) + toff);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+          if (P.on[j]) {                        // uniform over the wave
+            const uint32_t words[4] = {cur.bw[j].x, cur.bw[j].y, cur.bw[j].z, cur.bw[j].w};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              float e[4][2];
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  const uint32_t r = __builtin_amdgcn_alignbit(words[a], words[a], rot[k][h]);
+                  e[k][h] = lut_at(lut, ((r & 0x1E000u) | nbase[k][h]) + toff);
+                }
+              const float sm = ((e[0][0] + e[0][1]) + (e[1][0] + e[1][1])) +
+                               ((e[2][0] + e[2][1]) + (e[3][0] + e[3][1]));
+              acc[j][a] = __builtin_fmaf(h2f(cur.aw[j][a >> 1], a & 1), sm, acc[j][a]);
+            }
+            if constexpr (OFF) {
+              if (P.q0[j]) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                  acc[j][a] = __builtin_fmaf(h2f(cur.ow[j][a >> 1], a & 1), csum, acc[j][a]);
+              }
+            }
+          }
+        }
+      }
+      load_units<Q, OFF, UPW>(p, l, P, ic, cur);
+    }
+  }
+  __syncthreads();                              // every lookup done: the tables are free
+  float* red = lut;
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int u = l.wave + 16 * j;
+    if (P.on[j]) {
+      const float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      const float t = row_sum16(v, l.lane);
+      if (holds_row_sum(l.lane)) red[u * kRowTile + reduced_row(l.lane)] = t;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ri * kRowTile; idx += 1024) {
+    const int rtl = idx / kRowTile, row = idx - rtl * kRowTile;
+    float sum = red[(rtl * Q) * kRowTile + row];
+#pragma unroll
+    for (int q = 1; q < Q; ++q) sum += red[(rtl * Q + q) * kRowTile + row];
+    const int n = (rt0 + rtl) * kRowTile + row;
+    if (n < p.N) p.y[n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  }
+}
+
 // ------------------------------------------------------------------ instances
 
 using KernelFn = void (*)(Params);
@@ -984,6 +1302,38 @@ KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool 
   if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl, pr, ei, once);
   return nullptr;
 }
+
+// Nibble-table instances: (units per wave, ring depth) with the ring dividing
+// the 16 tiles of a phase: (1, 8), (2, 4), (3, 2), (4, 2), plus (1, 4) and
+// (2, 2) for tuning; nr = 0 picks the deepest for upw.
+template <int Q>
+KernelFn nibble_kernel_of_q(bool off, int upw, int nr) {
+  if (upw == 1) {
+    if (nr == 4) return off ? lutgemv_nibble_kernel<Q, true, 1, 4> : lutgemv_nibble_kernel<Q, false, 1, 4>;
+    if (nr == 0 || nr == 8)
+      return off ? lutgemv_nibble_kernel<Q, true, 1, 8> : lutgemv_nibble_kernel<Q, false, 1, 8>;
+  } else if (upw == 2) {
+    if (nr == 2) return off ? lutgemv_nibble_kernel<Q, true, 2, 2> : lutgemv_nibble_kernel<Q, false, 2, 2>;
+    if (nr == 0 || nr == 4)
+      return off ? lutgemv_nibble_kernel<Q, true, 2, 4> : lutgemv_nibble_kernel<Q, false, 2, 4>;
+  } else if (upw == 3) {
+    if (nr == 0 || nr == 2)
+      return off ? lutgemv_nibble_kernel<Q, true, 3, 2> : lutgemv_nibble_kernel<Q, false, 3, 2>;
+  } else if (upw == 4) {
+    if (nr == 0 || nr == 2)
+      return off ? lutgemv_nibble_kernel<Q, true, 4, 2> : lutgemv_nibble_kernel<Q, false, 4, 2>;
+  }
+  return nullptr;
+}
+
+extern template KernelFn nibble_kernel_of_q<1>(bool, int, int);
+extern template KernelFn nibble_kernel_of_q<2>(bool, int, int);
+extern template KernelFn nibble_kernel_of_q<3>(bool, int, int);
+extern template KernelFn nibble_kernel_of_q<4>(bool, int, int);
+extern template KernelFn nibble_kernel_of_q<5>(bool, int, int);
+extern template KernelFn nibble_kernel_of_q<6>(bool, int, int);
+extern template KernelFn nibble_kernel_of_q<7>(bool, int, int);
+extern template KernelFn nibble_kernel_of_q<8>(bool, int, int);
 
 extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, bool, bool, bool);
 extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, bool, bool, bool);

@@ -8,4 +8,5 @@
 
 namespace lutgemm {
 template KernelFn kernels_of_q<LUTGEMM_Q>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+template KernelFn nibble_kernel_of_q<LUTGEMM_Q>(bool, int, int);
 }  // namespace lutgemm

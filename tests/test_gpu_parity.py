@@ -312,11 +312,11 @@ def test_xcd_grouped_batch_groups_all_outputs(monkeypatch, tile, N, K, m):
 def test_workspace_reuse_across_shapes():
     """One workspace (through the C ABI) serves a large split call, then a smaller
     one, then the large again: each completed call leaves its counters zero."""
-    big = workloads.random_bcq(8192, 12288, 3, 128, m=1, seed=6)
+    big = workloads.random_bcq(8192, 12288, 3, 128, m=2, seed=6)
     small = workloads.random_bcq(1024, 4096, 2, 64, m=3, seed=7)
     pb = lg.PackedBCQ.from_bcq(big.bits, big.alpha, None, big.g)
     ps = lg.PackedBCQ.from_bcq(small.bits, small.alpha, None, small.g)
-    nb = lg.workspace_size(big.N, big.K, big.q, big.g, False, 1)
+    nb = lg.workspace_size(big.N, big.K, big.q, big.g, False, 2)
     ns = lg.workspace_size(small.N, small.K, small.q, small.g, False, 3)
     assert nb > 0 and ns > 0
     ws = torch.empty(max(nb, ns), dtype=torch.uint8, device=DEV)
@@ -432,8 +432,8 @@ def test_maximum_split_all_outputs(monkeypatch):
 def test_two_streams_share_a_weight():
     """Split launches of one weight on two streams at once: each stream has its
     own workspace, and both results match the oracle."""
-    w = workloads.random_bcq(6144, 12288, 3, 128, m=1, seed=44)
-    assert lg.workspace_size(w.N, w.K, w.q, w.g, False, 1) > 0
+    w = workloads.random_bcq(6144, 12288, 3, 128, m=2, seed=44)
+    assert lg.workspace_size(w.N, w.K, w.q, w.g, False, 2) > 0
     pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
     x = torch.from_numpy(w.x).to(DEV)
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
@@ -487,3 +487,49 @@ def test_stream_read_probe_runs():
     assert (sink == 0).all()
     with pytest.raises(lg.LutGemmError):
         lg.stream_read(src.data_ptr() + 8, n - 16, sink.data_ptr(), sink.numel(), True, sh)
+
+
+# the nibble-table unit kernel (batch 1, few row tiles per compute unit):
+# "0,1,16,1,NR,RI,1,0,0,1" forces it with RI row tiles per workgroup and ring depth NR
+@pytest.mark.parametrize("N,K,q,g,off,ri,nr", [
+    (11008, 4096, 4, 128, True, 3, 0),     # the int4 MLP shape: one plane-0 unit per row tile
+    (3000, 4128, 3, 32, True, 2, 8),       # ragged rows and a ragged last input tile
+    (3000, 4128, 3, 32, True, 5, 4),       # units 0..14 with 16 waves: one wave idle
+    (777, 15360, 4, 64, True, 7, 4),       # the largest x staged in LDS, two units per wave
+    (777, 15360, 4, 64, True, 7, 2),
+    (64, 512, 1, 32, False, 1, 8),         # one input tile: fewer tiles than ring steps
+    (1000, 8192, 8, 8192, True, 2, 0),     # row-wise groups (one group per row), q = 8
+    (1000, 8192, 8, 8192, True, 7, 0),     # 56 units: four per wave
+    (2000, 2048, 5, 256, False, 4, 0),     # two groups per input tile
+    (500, 3072, 2, 1024, True, 6, 0),      # groups wider than an input tile
+    (900, 7680, 6, 1536, True, 3, 2),      # groups of three input tiles, 18 units
+    (512, 512, 3, 128, False, 1, 0),       # one row tile per workgroup, one input tile
+    (6144, 12288, 3, 128, False, 2, 0),    # the one-of-eight row shard of the FFN-up matrix
+])
+def test_unit_kernel_all_outputs(monkeypatch, N, K, q, g, off, ri, nr):
+    """The nibble-table unit kernel: 4-input tables built per phase of 8192
+    inputs (15360 inputs: two phases), forced with RI row tiles per workgroup
+    and ring depth NR (0: its default)."""
+    w = workloads.random_bcq(N, K, q, g, m=1, seed=N + K + q + ri, with_offset=off,
+                             x_dist="student_t" if q % 2 else "normal",
+                             name=f"units_{N}x{K}q{q}g{g}ri{ri}nr{nr}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", f"0,1,16,1,{nr},{ri},1,0,0,1")
+    _say(f"unit kernel RI={ri} NR={nr}: N={N} K={K} q={q} g={g} offset={off}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
+def test_unit_kernel_declined_by_override(monkeypatch):
+    """US = 0 in the override gives the dispatcher's choice without the unit
+    kernel (split reduction here); both agree with the oracle."""
+    w = workloads.random_bcq(6144, 12288, 3, 128, m=1, seed=46)
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, None, w.g)
+    ref = oracle.gemv(w.bits, w.alpha, None, w.x, w.g)
+    _say("unit kernel declined")
+    y_units = _gpu_y(pw, w.x)
+    monkeypatch.setenv("LUTGEMM_TILE", "0,0,0,0,0,0,-1,-1,-1,0")
+    y_split = _gpu_y(pw, w.x)
+    monkeypatch.delenv("LUTGEMM_TILE")
+    _check(y_units, w, ref=ref)
+    _check(y_split, w, ref=ref)

@@ -59,7 +59,7 @@ def test_noalloc_two_calls_second_smaller():
     smaller one (fewer rows, shorter input, another batch), both correct."""
     scratch = lg.noalloc_scratch_bytes()
     assert scratch == 4 << 20
-    big = workloads.random_bcq(6144, 12288, 3, 128, m=1, seed=51, name="noalloc_big")
+    big = workloads.random_bcq(6144, 12288, 3, 128, m=2, seed=51, name="noalloc_big")
     small = workloads.random_bcq(1000, 4104, 2, 24, m=3, seed=52, with_offset=True,
                                  name="noalloc_small")
     for w in (big, small):
