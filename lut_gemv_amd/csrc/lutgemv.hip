@@ -198,13 +198,16 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
     // eff: cost of one input tile per unit of (row tiles x batch rows) / 16;
     // bar: cost of one input tile per batch row of the item (barriers and
     // table builds that serialise); min_m: smallest batch the candidate is
-    // considered for. Measured on 12288 x 12288, m = 4..32: paired tables lost
-    // to 16 waves x 1 row at m = 4, and 16-wave paired instances to 8-wave ones
-    // at m = 8 (they win from m = 12 on).
+    // considered for. 16-wave paired tables (two batch rows per item, the
+    // weights read once for both) are considered from m = 2: with the split
+    // this model picks they measured 9-27% faster than 16 waves x 1 row at
+    // m = 2..10 (12288 x 12288: 24.9 -> 22.2 us at m = 2, 39.5 -> 34.6 at 4,
+    // 68.3 -> 53.8 at 8; 49152 x 12288 at m = 4: 130.2 -> 103.1), the same at
+    // m = 16, and the model keeps 16 x 1 at odd m = 3, 5.
     struct Cand { int w, rpw, mc; double eff, bar; bool pr; int min_m; };
     const Cand cands[] = {
         {16, 2, 1, 1.0, 0.0, false, 1},    {16, 1, 1, 1.0, 0.0, false, 1},
-        {16, 1, 2, 0.5, 0.28, true, 12},   {8, 2, 4, 0.5, 0.425, true, 8},
+        {16, 1, 2, 0.5, 0.28, true, 2},   {8, 2, 4, 0.5, 0.425, true, 8},
         {8, 1, 4, 0.5, 0.425, true, 8},    {8, 2, 2, 0.5, 0.425, true, 8},
         {8, 1, 2, 0.5, 0.425, true, 8},    {8, 2, 4, 0.71, 0.31, false, 4},
         {8, 1, 4, 0.71, 0.31, false, 4},   {8, 2, 2, 0.71, 0.31, false, 2},
