@@ -76,16 +76,18 @@ def kernel_hash():
 
 
 def stored_traffic(workload):
-    """HBM bytes per launch from rocprofv3 counters, if taken on this kernel source
-    and this workload."""
+    """HBM bytes per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE,
+    each scaled by what it reads for a copy of known size), if they were taken on
+    this kernel source for this workload; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash() or t.get("workload") != workload:
+    if t.get("kernel_sha256_16") != kernel_hash():
         return None
-    return t.get("bytes_per_launch")
+    rec = t.get("workloads", {}).get(workload)
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def cpu_baseline(w, threads, budget_s):
