@@ -356,6 +356,12 @@ def main():
                           f"{full1:.2f} s/GEMV ({nbytes / full1 / 1e9:.4f} GB/s)")}
         log(f"cpu baseline: {cpu['sample']}")
 
+    plan = None
+    if args.kernel == "lut":
+        # the launch lutgemm_run makes here (after LUTGEMM_TILE, if set)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        ws = None if cus == 256 else lg.workspace_size(w.N, w.K, w.q, w.g, bool(has_off), w.m)
+        plan = lg.query_plan(w.N, w.K, w.q, w.g, bool(has_off), w.m, cus=cus, workspace_bytes=ws)
     out = {
         "metric": (METRIC if w.name == "opt175b_ffn_up" and args.kernel == "lut"
                    else f"us/GEMV + achieved HBM GB/s, {w.name}, {args.kernel} kernel"),
@@ -380,7 +386,8 @@ def main():
                    "N": w.N, "K": w.K, "q": w.q, "g": w.g, "m": w.m,
                    "offset": bool(has_off), "x": "fp16", "y": "fp16",
                    "weights": f"{w.q} sign planes + fp16 scales per {w.g} inputs",
-                   "rotating_copies": R, "algorithmic_bytes": nbytes},
+                   "rotating_copies": R, "algorithmic_bytes": nbytes,
+                   "plan": plan},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

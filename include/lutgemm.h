@@ -201,6 +201,47 @@ int lutgemm_run_noalloc(const lutgemm_shape* s, int32_t m, const void* d_bits,
  * Never fails; host only. */
 size_t lutgemm_noalloc_scratch_bytes(void);
 
+/* The launch chosen for shape *s and batch m on a device with `cus` compute
+ * units, its split limited to `workspace_bytes` of workspace, after the
+ * LUTGEMM_TILE override if set. lutgemm_run's launch is the plan for
+ * (256, SIZE_MAX) on a full 256-CU MI355X and for (the device's count, the
+ * workspace passed) on any other; lutgemm_run_noalloc's is the plan for (the
+ * device's count, lutgemm_noalloc_scratch_bytes()). For tracing and tuning;
+ * host only, no HIP call.
+ * Table kinds (the card's section "Interesting ideas: Lookup tables instead of
+ * multiplications" defines the 256-entry table of an 8-input chunk):
+ *   LUTGEMM_TABLES_SINGLE  one table per batch row, two buffers;
+ *   LUTGEMM_TABLES_PAIRED  the tables of two batch rows interleaved entry by
+ *                          entry, one buffer;
+ *   LUTGEMM_TABLES_HALF    as paired, holding only the 128 entries with bit 7
+ *                          clear (entry b ^ 0xFF is minus entry b), two buffers;
+ *   LUTGEMM_TABLES_NIBBLE  16-entry tables of 4-input halves of each chunk,
+ *                          a byte's entry being the sum of its two halves'.
+ * Fields of a plan with no launch (m == 0, N == 0 or K == 0) are zero.
+ * Errors: NULL when s or out is NULL, SHAPE as for lutgemm_run or when
+ * cus < 1, INTERNAL when no kernel instance fits. */
+enum {
+  LUTGEMM_TABLES_SINGLE = 0,
+  LUTGEMM_TABLES_PAIRED = 1,
+  LUTGEMM_TABLES_HALF = 2,
+  LUTGEMM_TABLES_NIBBLE = 3
+};
+typedef struct lutgemm_plan {
+  int32_t tables;         /* LUTGEMM_TABLES_*                                   */
+  int32_t waves;          /* wave64s per workgroup                              */
+  int32_t rows_per_wave;  /* row tiles (16 rows) a wave looks up per step       */
+  int32_t batch_rows;     /* batch rows per work item                           */
+  int32_t row_tiles;      /* row tiles per work item                            */
+  int32_t split;          /* workgroups sharing one row block's input dimension */
+  int32_t x_in_lds;       /* 1: the whole of x is staged in LDS once            */
+  int32_t reserved;
+  int64_t items;          /* work items (row block, batch group, split)         */
+  int64_t workgroups;     /* workgroups launched                                */
+  uint64_t workspace_bytes;
+} lutgemm_plan;
+int lutgemm_query_plan(const lutgemm_shape* s, int32_t m, int32_t cus, size_t workspace_bytes,
+                       lutgemm_plan* out);
+
 /* Storage in bits of the matrix of shape *s: q sign bits per weight, one fp16
  * scale per (plane, row, group of g) and one fp16 offset per (row, group) when
  * s->has_offset (Elamur card, section "Interesting ideas: Group size as a

@@ -22,7 +22,7 @@ __all__ = [
     "check_shape", "packed_sizes", "workspace_size", "workspace_init",
     "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "footprint_bits",
     "search_group_sizes", "bcq_quantize", "stream_read", "lutgemm_run_noalloc",
-    "noalloc_scratch_bytes", "PackedBCQ", "STATUS",
+    "noalloc_scratch_bytes", "query_plan", "TABLES", "PackedBCQ", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,18 @@ class LutGemmError(RuntimeError):
         self.status = status
         self.name = STATUS.get(status, f"status {status}")
         super().__init__(f"{where}: {self.name} ({status_string(status)})")
+
+
+TABLES = {0: "single", 1: "paired", 2: "half", 3: "nibble"}
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("tables", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("rows_per_wave", ctypes.c_int32), ("batch_rows", ctypes.c_int32),
+                ("row_tiles", ctypes.c_int32), ("split", ctypes.c_int32),
+                ("x_in_lds", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("items", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_uint64)]
 
 
 class Shape(ctypes.Structure):
@@ -104,6 +116,9 @@ def lib() -> ctypes.CDLL:
     L.lutgemm_noalloc_scratch_bytes.argtypes = []
     L.lutgemm_stream_read.restype = ctypes.c_int
     L.lutgemm_stream_read.argtypes = [_P, _SZ, _P, _SZ, ctypes.c_int, _P]
+    L.lutgemm_query_plan.restype = ctypes.c_int
+    L.lutgemm_query_plan.argtypes = [_SHP, ctypes.c_int32, ctypes.c_int32, _SZ,
+                                     ctypes.POINTER(_Plan)]
     _LIB = L
     return L
 
@@ -234,6 +249,19 @@ def lutgemm_run_noalloc(shape: Shape, m: int, d_bits: int, d_alpha: int, d_offse
 def noalloc_scratch_bytes() -> int:
     """Bytes of the per-GPU scratch array of :func:`lutgemm_run_noalloc`."""
     return lib().lutgemm_noalloc_scratch_bytes()
+
+
+def query_plan(N: int, K: int, q: int, g: int, has_offset: bool, m: int, cus: int = 256,
+               workspace_bytes: Optional[int] = None) -> dict:
+    """The launch chosen for this shape and batch on `cus` compute units with its
+    split limited to `workspace_bytes` (None: unlimited); host only."""
+    pl = _Plan()
+    ws = (1 << 64) - 1 if workspace_bytes is None else int(workspace_bytes)
+    _check(lib().lutgemm_query_plan(ctypes.byref(_shape(N, K, q, g, has_offset)), int(m), int(cus),
+                                    ws, ctypes.byref(pl)), "lutgemm_query_plan")
+    d = {f: int(getattr(pl, f)) for f, _ in _Plan._fields_ if f != "reserved"}
+    d["tables"] = TABLES[d["tables"]]
+    return d
 
 
 def footprint_bits(N: int, K: int, q: int, g: int, has_offset: bool = False) -> int:

@@ -42,11 +42,11 @@ __global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
 // ------------------------------------------------------------------ dispatch
 
 // ring: >= 3 asks for the deeper ring where an instance has one, 0 for the
-// default; xl: the variant with x staged in LDS (batch 1); pr: paired tables;
-// ei: the early-issue ring of the x-in-LDS variant; once: read-once
-// (non-temporal) sign-plane loads at batch 1 without x in LDS.
+// default; xl: the variant with x staged in LDS (batch 1); pr: 1 paired tables,
+// 2 half paired tables; ei: the early-issue ring of the x-in-LDS variant; once:
+// read-once (non-temporal) sign-plane loads at batch 1 without x in LDS.
 KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring, bool xl,
-                     bool pr = false, bool ei = false, bool once = false) {
+                     int pr = 0, bool ei = false, bool once = false) {
   switch (q) {
     case 1: return kernels_of_q<1>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
     case 2: return kernels_of_q<2>(rpw, mc, gq, off, w, ring, xl, pr, ei, once);
@@ -82,7 +82,8 @@ struct Config {
   int RI;                // row tiles per row block (<= W * RPW)
   int ring;              // >= 3: the deeper ring; 0: the instance's default
   bool xl;               // x staged in LDS
-  bool pr;               // paired tables (two batch rows per table entry)
+  int pr;                // 1: paired tables (two batch rows per table entry), 2: half
+                         // paired tables (double-buffered), 0: neither
   bool ei;               // early-issue ring (x in LDS, two register sets)
   bool once;             // batch 1 without x in LDS: non-temporal sign-plane loads
   bool us;               // the nibble-table unit kernel (batch 1, few row tiles per CU)
@@ -104,8 +105,9 @@ struct TileOverride {
 
 // Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR[,EI[,US]]]]]]]]" (LUTGEMM_TILE);
 // never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
-// (default: where possible). PR: 1 paired tables where an instance has them, 0
-// never (default: the dispatcher's choice). EI: 1 the early-issue ring where
+// (default: where possible). PR: 1 paired tables where an instance has them, 2
+// half paired tables where an instance has them, 0 never (default: the
+// dispatcher's choice). EI: 1 the early-issue ring where
 // x is staged in LDS with the default ring, 0 never (the default). US: 1 the
 // nibble-table unit kernel where it applies (batch 1, scale groups dividing or
 // multiples of 512 inputs, x in LDS) with RI row tiles per workgroup (default:
@@ -145,7 +147,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
   c.W = 0;   // stays 0 if no instance fits (reported as an internal error)
   c.ring = 0;
   c.xl = false;
-  c.pr = false;
+  c.pr = 0;
   c.ei = false;
   c.once = false;
   const int q = (int)G.q;
@@ -204,7 +206,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
     // m = 2..10 (12288 x 12288: 24.9 -> 22.2 us at m = 2, 39.5 -> 34.6 at 4,
     // 68.3 -> 53.8 at 8; 49152 x 12288 at m = 4: 130.2 -> 103.1), the same at
     // m = 16, and the model keeps 16 x 1 at odd m = 3, 5.
-    struct Cand { int w, rpw, mc; double eff, bar; bool pr; int min_m; };
+    struct Cand { int w, rpw, mc; double eff, bar; int pr; int min_m; };
     const Cand cands[] = {
         {16, 2, 1, 1.0, 0.0, false, 1},    {16, 1, 1, 1.0, 0.0, false, 1},
         {16, 1, 2, 0.5, 0.28, true, 2},   {8, 2, 4, 0.5, 0.425, true, 8},
@@ -274,7 +276,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
   } else if (have_o) {
     const int w = o.w ? o.w : c.W;
     const int mc = o.mc ? o.mc : c.MC;
-    const bool pr = o.pr > 0;
+    const int pr = o.pr == 1 || o.pr == 2 ? o.pr : 0;
     const bool xl = pr ? false
                     : o.xl < 0 ? xl_ok && pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, true)
                                : (o.xl > 0 && xl_ok);
@@ -534,6 +536,38 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
       if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
     }
     return launch(G, m, c, cus, d_bits, d_alpha, d_offset, d_x, d_y, d_workspace, strm);
+  } catch (...) {
+    return LUTGEMM_ERR_INTERNAL;
+  }
+}
+
+int lutgemm_query_plan(const lutgemm_shape* s, int32_t m, int32_t cus, size_t workspace_bytes,
+                       lutgemm_plan* out) {
+  try {
+    if (!s || !out) return LUTGEMM_ERR_NULL;
+    int st = check_shape(s);
+    if (st) return st;
+    if (m < 0 || m > kMaxBatch || cus < 1) return LUTGEMM_ERR_SHAPE;
+    const Geometry G = geometry(s);
+    if (!buffers_fit(G, m)) return LUTGEMM_ERR_SHAPE;
+    *out = lutgemm_plan{};
+    if (m == 0 || G.N == 0 || G.K == 0) return LUTGEMM_OK;
+    const Config c = choose_config(G, m, cus, workspace_bytes);
+    if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
+    out->tables = c.us ? LUTGEMM_TABLES_NIBBLE
+                  : c.pr == 2 ? LUTGEMM_TABLES_HALF
+                  : c.pr == 1 ? LUTGEMM_TABLES_PAIRED
+                              : LUTGEMM_TABLES_SINGLE;
+    out->waves = c.W;
+    out->rows_per_wave = c.RPW;
+    out->batch_rows = c.MC;
+    out->row_tiles = c.RI;
+    out->split = c.S;
+    out->x_in_lds = c.xl ? 1 : 0;
+    out->items = c.n_rb * c.n_bg * c.S;
+    out->workgroups = c.us ? out->items : (out->items < cus ? out->items : cus);
+    out->workspace_bytes = c.ws_bytes;
+    return LUTGEMM_OK;
   } catch (...) {
     return LUTGEMM_ERR_INTERNAL;
   }

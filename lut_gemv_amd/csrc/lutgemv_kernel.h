@@ -210,6 +210,9 @@ struct LaneCtx {
   uint32_t tsel[4];   // (table index 4*c4 + b_k) * 4: byte 0 of the address
   uint32_t psel[4];   // v_perm selector taking byte b_k of a sign word into byte 1
   uint32_t ptsel[4];  // paired tables: bytes 0 and 2 of the address of chunk 4*c4 + b_k
+  uint32_t hsel[4];   // half tables: byte 0 of the address of chunk 4*c4 + b_k
+  uint32_t hmask;     // half tables: 0x80808080 for the lanes of chunks 32..63, else 0
+  uint32_t rot8;      // 8 * r4: rotating a sign word right by this puts byte b_k in byte k
   uint32_t aoff, ooff;  // g % 32 == 0 and g divides 512: byte offset of this lane's
                         // scales (and offsets) in a tile's scale block
 };
@@ -231,7 +234,10 @@ __device__ __forceinline__ LaneCtx lane_ctx() {
     l.psel[k] = 0x0C020000u | ((4u + b) << 8);
     const uint32_t t = 4u * (uint32_t)l.c4 + b;
     l.ptsel[k] = ((t & 31u) << 3) | ((t >> 5) << 16);
+    l.hsel[k] = (t & 31u) << 3;
   }
+  l.hmask = (l.lane >> 5) ? 0x80808080u : 0u;
+  l.rot8 = 8u * (uint32_t)l.r4;
   return l;
 }
 
@@ -560,6 +566,134 @@ __device__ __forceinline__ void lookups_pair(const LaneCtx& l, int h, const floa
   }
 }
 
+// ------------------------------------------------------------------ half tables
+// Complementing all eight signs negates an entry: entry (b ^ 0xFF) = -entry b.
+// A half table keeps only the 128 entries whose bit 7 is clear; a byte b with
+// bit 7 set reads entry b ^ 0xFF and takes it negated. A half-size paired table
+// (64 KiB for the 64 chunks of an input tile, two batch rows per entry) leaves
+// room for two buffers, so the next pair's table is built while the current
+// one is read, with one barrier per step instead of the paired tables' two.
+// The price is paid per lookup: folding the byte and applying its sign.
+// Layout: the pair of entry c < 128 of chunk t in buffer `buf` is at byte
+//   c*256 + (t / 32)*32 KiB + (t % 32)*8 + buf*64 KiB,
+// so bits 8-14 of an address are c and bit 15 is t / 32. Any byte in bits 8-15
+// gives an address inside the 128 KiB. As with the paired tables, the bank of
+// an entry depends only on t % 32: the reads are free of bank conflicts.
+
+// Half paired table of lane l's chunk into buffer `buf`: the entries whose bits
+// NB..6 equal the wave index (NB = 3 with 16 waves, 4 with 8), walked in
+// Gray-code order of bits 0..NB-1 as in build_table. Entry c (bit 7 clear) is
+// sum_{t<7} (bit t of c ? +x_t : -x_t) - x_7.
+template <int W>
+__device__ __forceinline__ void build_half_pair(float* lut, int buf, const LaneCtx& l,
+                                                const uint4 xa, const uint4 xb) {
+  constexpr int NB = W == 16 ? 3 : 4;
+  static_assert(W == 8 || W == 16, "8 or 16 waves per workgroup");
+  float x[8], y[8];
+  unpack8(xa, x);
+  unpack8(xb, y);
+  const int h0 = l.wave << NB;
+  float T = -x[7], U = -y[7];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    if (j < NB) {
+      T -= x[j];
+      U -= y[j];
+    } else {
+      const bool on = ((h0 >> j) & 1) != 0;
+      T += on ? x[j] : -x[j];
+      U += on ? y[j] : -y[j];
+    }
+  }
+  float twx[NB], twy[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    twx[t] = x[t] + x[t];
+    twy[t] = y[t] + y[t];
+  }
+  char* base = reinterpret_cast<char*>(lut) + buf * (kLutWords * 4) + h0 * 256 +
+               (l.lane >> 5) * 32768 + (l.lane & 31) * 8;
+  *reinterpret_cast<float2*>(base) = make_float2(T, U);
+#pragma unroll
+  for (int n = 1; n < (1 << NB); ++n) {
+    const int t = __builtin_ctz(n);
+    const int pat = n ^ (n >> 1);
+    T += ((pat >> t) & 1) ? twx[t] : -twx[t];
+    U += ((pat >> t) & 1) ? twy[t] : -twy[t];
+    *reinterpret_cast<float2*>(base + pat * 256) = make_float2(T, U);
+  }
+}
+
+// Lookups of batch rows 2h and 2h+1 from the half paired table in buffer `buf`
+// (grouped scales). Per sign word (four chunk bytes of one row): rotate it so
+// that byte k is the byte of visit k; a v_perm with sign-extending selectors
+// gives 0xFF in each byte whose bit 7 is set, and xor with that folds every
+// byte below 128 (the chunk half goes into bit 7). The sign of a byte is put on
+// the row's fp16 scale (bit 15 or 31 of its scale word), so that each entry is
+// accumulated with one fma per batch row.
+template <int Q, int RPW, int MC, bool OFF>
+__device__ __forceinline__ void lookups_half(const LaneCtx& l, int h, int buf, const float* lut,
+                                             const TileRegs<Q, RPW, MC, true, OFF>& T,
+                                             float (&acc)[MC][RPW][4]) {
+  const int r0 = 2 * h, r1 = 2 * h + 1;
+  const uint32_t bb = (uint32_t)buf << 16;
+  uint32_t hs[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) hs[k] = l.hsel[k] | bb;
+  float cs0 = 0.f, cs1 = 0.f;
+  if constexpr (OFF) {
+    // entry 0xFF (the sum of a chunk's 8 inputs) is minus half-table entry 0
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 e = lut_at2(lut, hs[k] | (l.hmask & 0x8000u));
+      cs0 -= e.x;
+      cs1 -= e.y;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    if (i < T.pos.c.valid_rpw) {  // uniform over the wave
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint32_t words[4] = {T.bw[i][q].x, T.bw[i][q].y, T.bw[i][q].z, T.bw[i][q].w};
+        uint32_t wr[4];
+        float2 e[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          wr[a] = __builtin_amdgcn_alignbit(words[a], words[a], l.rot8);
+          const uint32_t neg = __builtin_amdgcn_perm(wr[a] << 8, wr[a], 0x090B080Au);
+          const uint32_t wf = (wr[a] ^ neg) | l.hmask;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            e[a][k] = lut_at2(lut, __builtin_amdgcn_perm(wf, hs[k], 0x0C020000u | ((4u + k) << 8)));
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const uint32_t aword = T.aw[i][q * 2 + (a >> 1)];
+          // the row's scale is bits 16-31 (a odd) or 0-15 (a even) of aword
+          constexpr int kPos[2] = {15, 31};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int pos = kPos[a & 1], src = 8 * k + 7;
+            const uint32_t sgn = pos >= src ? wr[a] << (pos - src) : wr[a] >> (src - pos);
+            const float al = h2f(aword ^ (sgn & (1u << pos)), a & 1);
+            acc[r0][i][a] = __builtin_fmaf(al, e[a][k].x, acc[r0][i][a]);
+            acc[r1][i][a] = __builtin_fmaf(al, e[a][k].y, acc[r1][i][a]);
+          }
+        }
+      }
+      if constexpr (OFF) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float o = h2f(T.ow[i][a >> 1], a & 1);
+          acc[r0][i][a] = __builtin_fmaf(o, cs0, acc[r0][i][a]);
+          acc[r1][i][a] = __builtin_fmaf(o, cs1, acc[r1][i][a]);
+        }
+      }
+    }
+  }
+}
+
 // Sum each of a lane's four row accumulators (rows 4*r4 + a) over the 16
 // lanes that share its row quad (lanes differing in bits 0-2 and 5), with
 // cross-lane moves that do not go through LDS: v_permlane32_swap exchanges the
@@ -714,8 +848,11 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // the lookups stay exact (they would otherwise also wait for the tile ahead).
 // ONCE (batch 1 without x in LDS): each sign byte is read once per product, and
 // its loads are non-temporal as they are with XL.
+// HT (with PR): half paired tables in two buffers; each step (one pair of
+// batch rows of one tile) looks up one buffer, builds the next step's table in
+// the other and ends at the step's one barrier.
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL, bool PR = false,
-          bool EI = false, bool ONCE = false>
+          bool EI = false, bool ONCE = false, bool HT = false>
 // The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
 // also the most that can ever run; saying so lets the scheduler use the
 // whole register budget to keep table lookups in flight.
@@ -725,6 +862,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   static_assert(!PR || (GQ && !XL && MC % 2 == 0), "paired tables: grouped scales, even MC");
   static_assert(!EI || (XL && NR == 2 && !PR), "early issue: x in LDS, two register sets");
   static_assert(!ONCE || (!XL && !PR && MC == 1), "read-once loads: batch 1 without x in LDS");
+  static_assert(!HT || PR, "half tables are paired");
   __shared__ float lut[2 * kLutWords];
   __shared__ uint4 xs[XL ? kXChunks : 1];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
@@ -796,7 +934,42 @@ __global__ void __launch_bounds__(W * 64, W / 4)
       return T.xv[r];
     }
   };
-  if constexpr (PR) {
+  if constexpr (HT) {
+    int buf = 0;
+    build_half_pair<W>(lut, 0, l, R[0].xv[0], R[0].xv[1]);
+    __syncthreads();
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        if (!done) {
+          TR& cur = R[s];
+          TR& nxt = R[(s + 1) % NR];
+          TR& pre = R[(s + NR - 1) % NR];
+          pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
+          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
+#pragma unroll
+          for (int h = 0; h < MC / 2; ++h) {
+            if (2 * h < cur.pos.c.rows_here) {  // uniform over the workgroup
+              lookups_half<Q, RPW, MC, OFF>(l, h, buf, lut, cur, acc);
+              const int hn = 2 * h + 2 < MC ? 2 * h + 2 : 0;   // a constant once unrolled
+              if (2 * h + 2 < cur.pos.c.rows_here) {
+                build_half_pair<W>(lut, buf ^ 1, l, cur.xv[hn], cur.xv[hn + 1]);
+              } else if (nxt.pos.live) {
+                build_half_pair<W>(lut, buf ^ 1, l, nxt.xv[0], nxt.xv[1]);
+              }
+              __syncthreads();
+              buf ^= 1;
+            }
+          }
+          if (cur.pos.kt + 1 == cur.pos.c.kt1) finish_item<RPW, MC>(p, l, cur.pos.c, acc);
+          done = !nxt.pos.live;
+        }
+      }
+    }
+    if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    return;
+  } else if constexpr (PR) {
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -1222,12 +1395,21 @@ constexpr int kRingPair =
 // tables (grouped scales, even MC); ei the early-issue ring of the x-in-LDS
 // variant (default ring only); once the read-once (non-temporal) sign-plane
 // loads of the 16-wave batch-1 instances without x in LDS.
+// pr: 1 paired tables, 2 half paired tables (one row tile per wave only).
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
-KernelFn kernel_or_null(int ring, bool xl, bool pr, bool ei, bool once) {
+KernelFn kernel_or_null(int ring, bool xl, int pr, bool ei, bool once) {
   if (pr) {
     if constexpr (GQ && kRingPair<Q, RPW, MC, OFF, W> > 0) {
-      return xl ? nullptr
-                : lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true>;
+      if (xl) return nullptr;
+      if (pr == 2) {
+        if constexpr (RPW == 1) {
+          return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true,
+                                false, false, true>;
+        } else {
+          return nullptr;
+        }
+      }
+      return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true>;
     } else {
       return nullptr;
     }
@@ -1266,7 +1448,7 @@ KernelFn kernel_or_null(int ring, bool xl, bool pr, bool ei, bool once) {
 }
 
 template <int Q, int RPW, int MC, int W>
-KernelFn pick_flags(bool gq, bool off, int ring, bool xl, bool pr, bool ei, bool once) {
+KernelFn pick_flags(bool gq, bool off, int ring, bool xl, int pr, bool ei, bool once) {
   if (gq)
     return off ? kernel_or_null<Q, RPW, MC, true, true, W>(ring, xl, pr, ei, once)
                : kernel_or_null<Q, RPW, MC, true, false, W>(ring, xl, pr, ei, once);
@@ -1275,7 +1457,7 @@ KernelFn pick_flags(bool gq, bool off, int ring, bool xl, bool pr, bool ei, bool
 }
 
 template <int Q, int W>
-KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool pr, bool ei,
+KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, int pr, bool ei,
                      bool once) {
   if (mc == 1) {
     if (rpw == 2) return pick_flags<Q, 2, 1, W>(gq, off, ring, xl, pr, ei, once);
@@ -1293,10 +1475,10 @@ KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, bool
 // The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
 // item, scale groups aligned to 32 inputs (gq), an offset term (off), w waves
 // per workgroup, ring depth (0 default, >= 3 deeper), x in LDS (xl), paired
-// tables (pr), the early-issue ring (ei) and read-once sign-plane loads (once),
-// or nullptr if none is built.
+// tables (pr: 1 paired, 2 half paired), the early-issue ring (ei) and read-once
+// sign-plane loads (once), or nullptr if none is built.
 template <int Q>
-KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, bool pr,
+KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, int pr,
                       bool ei, bool once) {
   if (w == 16) return pick_rpw_mc<Q, 16>(rpw, mc, gq, off, ring, xl, pr, ei, once);
   if (w == 8) return pick_rpw_mc<Q, 8>(rpw, mc, gq, off, ring, xl, pr, ei, once);
@@ -1335,13 +1517,13 @@ extern template KernelFn nibble_kernel_of_q<6>(bool, int, int);
 extern template KernelFn nibble_kernel_of_q<7>(bool, int, int);
 extern template KernelFn nibble_kernel_of_q<8>(bool, int, int);
 
-extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, bool, bool, bool);
-extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, bool, bool, bool);
-extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool, bool, bool, bool);
-extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool, bool, bool, bool);
-extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool, bool, bool, bool);
-extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool, bool, bool, bool);
-extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool, bool, bool, bool);
-extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+extern template KernelFn kernels_of_q<1>(int, int, bool, bool, int, int, bool, int, bool, bool);
+extern template KernelFn kernels_of_q<2>(int, int, bool, bool, int, int, bool, int, bool, bool);
+extern template KernelFn kernels_of_q<3>(int, int, bool, bool, int, int, bool, int, bool, bool);
+extern template KernelFn kernels_of_q<4>(int, int, bool, bool, int, int, bool, int, bool, bool);
+extern template KernelFn kernels_of_q<5>(int, int, bool, bool, int, int, bool, int, bool, bool);
+extern template KernelFn kernels_of_q<6>(int, int, bool, bool, int, int, bool, int, bool, bool);
+extern template KernelFn kernels_of_q<7>(int, int, bool, bool, int, int, bool, int, bool, bool);
+extern template KernelFn kernels_of_q<8>(int, int, bool, bool, int, int, bool, int, bool, bool);
 
 }  // namespace lutgemm

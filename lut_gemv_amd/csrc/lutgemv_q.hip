@@ -7,6 +7,6 @@
 #endif
 
 namespace lutgemm {
-template KernelFn kernels_of_q<LUTGEMM_Q>(int, int, bool, bool, int, int, bool, bool, bool, bool);
+template KernelFn kernels_of_q<LUTGEMM_Q>(int, int, bool, bool, int, int, bool, int, bool, bool);
 template KernelFn nibble_kernel_of_q<LUTGEMM_Q>(bool, int, int);
 }  // namespace lutgemm

@@ -262,6 +262,28 @@ def test_paired_tables_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# PR = 2: half paired tables (entries with bit 7 clear, double-buffered); the
+# bytes with bit 7 set read the complementary entry negated
+@pytest.mark.parametrize("tile", ["1,1,16,2,0,16,0,2", "1,3,16,2,0,11,0,2", "1,1,8,4,0,8,0,2",
+                                  "1,2,8,2,0,5,0,2", "1,4,8,4,0,7,0,2"])
+@pytest.mark.parametrize("N,K,q,g,m,off", [
+    (1000, 4128, 3, 32, 3, True),      # ragged rows and input tiles, odd batch
+    (300, 1536, 5, 64, 5, False),
+    (1024, 12288, 3, 128, 4, False),
+    (129, 2048, 8, 256, 7, True),
+    (700, 1024, 2, 32, 1, True),       # one batch row: the pair's second row is zero
+    (513, 3072, 1, 512, 10, False),
+])
+def test_half_tables_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + q + m + 7, with_offset=off,
+                             name=f"half_{N}x{K}q{q}g{g}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", tile)
+    _say(f"half tables {tile}: N={N} K={K} q={q} g={g} m={m} offset={off}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
 # "RPW,S,W,MC,ring,RI,XL,PR,EI": x in LDS with the early-issue ring (EI = 1), forced
 # onto single-item, split and many-item launches, and the plain ring beside it (EI = 0)
 @pytest.mark.parametrize("tile", ["1,1,16,1,0,12,1,0,1", "1,1,16,1,0,12,1,0,0", "1,3,16,1,0,5,1,0,1",

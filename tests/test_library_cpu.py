@@ -86,6 +86,51 @@ def test_every_configuration_has_a_kernel(q, g):
                 lg.workspace_size(N, 4096 if 4096 % g == 0 else 24 * g, q, g, off, m)
 
 
+def test_query_plan_batch_one_and_batched():
+    """The launch plans of the benchmark's shapes on a full MI355X (host only)."""
+    c2 = lg.query_plan(49152, 12288, 3, 128, False, 1)
+    assert c2["tables"] == "single" and c2["waves"] == 16 and c2["x_in_lds"] == 1
+    assert c2["split"] == 1 and c2["items"] == 256 and c2["workgroups"] == 256
+    assert c2["row_tiles"] * 256 >= 49152 // 16 and c2["workspace_bytes"] == 0
+    for m in (2, 4, 16, 32):
+        p = lg.query_plan(12288, 12288, 3, 128, False, m)
+        assert p["tables"] == "paired" and p["batch_rows"] == 2 and p["x_in_lds"] == 0, (m, p)
+        assert p["workspace_bytes"] == lg.workspace_size(12288, 12288, 3, 128, False, m)
+        assert p["workgroups"] == min(p["items"], 256)
+    nib = lg.query_plan(4096, 4096, 3, 128, False, 1)
+    assert nib["tables"] == "nibble" and nib["split"] == 1 and nib["workgroups"] == nib["items"]
+    # scale groups not aligned to 32 inputs: single-row tables
+    assert lg.query_plan(4096, 3072, 3, 24, False, 4)["tables"] == "single"
+    for off in (False, True):
+        for m in (0, 1, 3, 8):
+            for N, K in ((0, 512), (512, 0)):
+                assert lg.query_plan(N, K, 3, 128 if K else 8, off, m)["waves"] == 0
+
+
+def test_query_plan_limits_and_override(monkeypatch):
+    shard = lg.query_plan(6144, 12288, 3, 128, False, 1)
+    assert shard["split"] > 1 and shard["workspace_bytes"] > 0
+    none = lg.query_plan(6144, 12288, 3, 128, False, 1, workspace_bytes=0)
+    assert none["split"] == 1 and none["workspace_bytes"] == 0
+    small = lg.query_plan(6144, 12288, 3, 128, False, 1, cus=80)
+    assert small["workgroups"] <= 80
+    monkeypatch.setenv("LUTGEMM_TILE", "1,4,16,2,0,16,0,2")
+    half = lg.query_plan(12288, 12288, 3, 128, False, 8)
+    assert (half["tables"], half["split"], half["batch_rows"], half["waves"]) == ("half", 4, 2, 16)
+    monkeypatch.setenv("LUTGEMM_TILE", "0,1,16,1,0,3,1,0,0,1")
+    assert lg.query_plan(11008, 4096, 4, 128, True, 1)["tables"] == "nibble"
+    monkeypatch.delenv("LUTGEMM_TILE")
+    L = lg.lib()
+    pl = lg._Plan()
+    shp = lg.Shape(512, 512, 3, 128, 0)
+    assert L.lutgemm_query_plan(None, 1, 256, 0, ctypes.byref(pl)) == 1
+    assert L.lutgemm_query_plan(ctypes.byref(shp), 1, 256, 0, None) == 1
+    assert L.lutgemm_query_plan(ctypes.byref(shp), 1, 0, 0, ctypes.byref(pl)) == 2
+    assert L.lutgemm_query_plan(ctypes.byref(shp), -1, 256, 0, ctypes.byref(pl)) == 2
+    bad = lg.Shape(512, 500, 3, 128, 0)
+    assert L.lutgemm_query_plan(ctypes.byref(bad), 1, 256, 0, ctypes.byref(pl)) == 2
+
+
 # ---------------------------------------------------------------- packing parity
 
 @pytest.mark.parametrize("N,K,q,g,off", [

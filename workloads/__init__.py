@@ -190,7 +190,7 @@ WORKLOADS = {
                          "x[1x4096]; W 11008x4096 uniform int4, zero 8, g=128 "
                          "-> BCQ q=4 + offset; seed 2"),
 }
-for _m in (4, 16, 32):
+for _m in (2, 4, 8, 16, 32):
     WORKLOADS[f"decode_m{_m}"] = (
         _decode(_m), f"x[{_m}x12288]; W 12288x12288 BCQ q=3 g=128; seeds 3/{30 + _m}")
 for _q in (1, 2, 4):
