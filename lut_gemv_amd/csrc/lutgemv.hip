@@ -43,7 +43,7 @@ __global__ void zero_bytes_kernel(uint8_t* p, size_t n) {
 
 // ring: >= 3 asks for the deeper ring where an instance has one, 0 for the
 // default; xl: the variant with x staged in LDS (batch 1); pr: 1 paired tables,
-// 2 half paired tables; ei: the early-issue ring of the x-in-LDS variant; once:
+// 2 half paired tables, 3 split paired tables; ei: the early-issue ring of the x-in-LDS variant; once:
 // read-once (non-temporal) sign-plane loads at batch 1 without x in LDS.
 KernelFn pick_kernel(int q, int rpw, int mc, bool gq, bool off, int w, int ring, bool xl,
                      int pr = 0, bool ei = false, bool once = false) {
@@ -83,7 +83,8 @@ struct Config {
   int ring;              // >= 3: the deeper ring; 0: the instance's default
   bool xl;               // x staged in LDS
   int pr;                // 1: paired tables (two batch rows per table entry), 2: half
-                         // paired tables (double-buffered), 0: neither
+                         // paired tables, 3: split paired tables (both double-buffered),
+                         // 0: neither
   bool ei;               // early-issue ring (x in LDS, two register sets)
   bool once;             // batch 1 without x in LDS: non-temporal sign-plane loads
   bool us;               // the nibble-table unit kernel (batch 1, few row tiles per CU)
@@ -105,8 +106,8 @@ struct TileOverride {
 
 // Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR[,EI[,US]]]]]]]]" (LUTGEMM_TILE);
 // never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
-// (default: where possible). PR: 1 paired tables where an instance has them, 2
-// half paired tables where an instance has them, 0 never (default: the
+// (default: where possible). PR: 1 paired tables, 2 half paired tables, 3
+// split paired tables, each where an instance has them, 0 never (default: the
 // dispatcher's choice). EI: 1 the early-issue ring where
 // x is staged in LDS with the default ring, 0 never (the default). US: 1 the
 // nibble-table unit kernel where it applies (batch 1, scale groups dividing or
@@ -276,7 +277,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
   } else if (have_o) {
     const int w = o.w ? o.w : c.W;
     const int mc = o.mc ? o.mc : c.MC;
-    const int pr = o.pr == 1 || o.pr == 2 ? o.pr : 0;
+    const int pr = o.pr >= 1 && o.pr <= 3 ? o.pr : 0;
     const bool xl = pr ? false
                     : o.xl < 0 ? xl_ok && pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, true)
                                : (o.xl > 0 && xl_ok);
@@ -555,6 +556,7 @@ int lutgemm_query_plan(const lutgemm_shape* s, int32_t m, int32_t cus, size_t wo
     const Config c = choose_config(G, m, cus, workspace_bytes);
     if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
     out->tables = c.us ? LUTGEMM_TABLES_NIBBLE
+                  : c.pr == 3 ? LUTGEMM_TABLES_SPLIT
                   : c.pr == 2 ? LUTGEMM_TABLES_HALF
                   : c.pr == 1 ? LUTGEMM_TABLES_PAIRED
                               : LUTGEMM_TABLES_SINGLE;

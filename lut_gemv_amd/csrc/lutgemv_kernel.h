@@ -210,7 +210,8 @@ struct LaneCtx {
   uint32_t tsel[4];   // (table index 4*c4 + b_k) * 4: byte 0 of the address
   uint32_t psel[4];   // v_perm selector taking byte b_k of a sign word into byte 1
   uint32_t ptsel[4];  // paired tables: bytes 0 and 2 of the address of chunk 4*c4 + b_k
-  uint32_t hsel[4];   // half tables: byte 0 of the address of chunk 4*c4 + b_k
+  uint32_t hsel[4];   // half tables and split paired tables: byte 0 of the address of
+                      // chunk 4*c4 + b_k, i.e. 8 * ((4*c4 + b_k) % 32)
   uint32_t hmask;     // half tables: 0x80808080 for the lanes of chunks 32..63, else 0
   uint32_t rot8;      // 8 * r4: rotating a sign word right by this puts byte b_k in byte k
   uint32_t aoff, ooff;  // g % 32 == 0 and g divides 512: byte offset of this lane's
@@ -731,6 +732,173 @@ __device__ __forceinline__ int reduced_row(int lane) {
 }
 __device__ __forceinline__ bool holds_row_sum(int lane) { return (lane & 6) == 4; }
 
+// ------------------------------------------------------------------ split paired tables
+// Paired tables (two batch rows per entry) of half an input tile: 32 chunks,
+// 64 KiB, so two buffers fit and each step builds the next table while it
+// reads the current one, with one barrier per step and no change to the
+// lookup itself. A tile is looked up in two steps, chunks 0-31 from buffer 0
+// and chunks 32-63 from buffer 1. The pair of entry p of chunk t of the half
+// is at byte p*256 + t*8 + buffer*64 KiB (row 2h in the low word). The bank of
+// an entry depends only on t, and the lanes of each half-wave read 32
+// different chunks: no bank conflicts.
+//
+// Lanes. The loads are those of the other kernels (lane l holds the lane block
+// of rows 4*r4..+3 and chunks 4*c4..+3, c4 = (l & 7) + 8*(l >> 5), and its
+// scales). In each step every lane looks up two rows of four chunks of the
+// current half: lane l takes rows 4*r4 + 2*rh + {0, 1} (rh = l >> 5) of
+// chunks 4*(l & 7)..+3 of the half. One v_permlane32_swap per register pair
+// moves the data there: after swapping the lower lanes of (words 2, 3) with
+// the upper lanes of (words 0, 1), words 0 and 1 hold the two rows of the
+// first half and words 2 and 3 those of the second. The same swap arranges
+// the scales (and offsets) of each plane.
+template <int Q, int MC, bool OFF>
+__device__ __forceinline__ void split_arrange(TileRegs<Q, 1, MC, true, OFF>& T) {
+  auto swap = [](uint32_t& lo, uint32_t& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+    lo = (uint32_t)r[0];
+    hi = (uint32_t)r[1];
+  };
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    swap(T.bw[0][q].x, T.bw[0][q].z);
+    swap(T.bw[0][q].y, T.bw[0][q].w);
+    swap(T.aw[0][2 * q], T.aw[0][2 * q + 1]);
+  }
+  if constexpr (OFF) swap(T.ow[0][0], T.ow[0][1]);
+}
+
+// Activations of the table of half H for batch rows (a, b): lane l gets chunk
+// (l & 31) + 32*H of row a (lanes 0-31) or of row b (lanes 32-63). The tile's
+// chunk l of each row is in lane l, so one swap per register gives both
+// halves.
+template <int H>
+__device__ __forceinline__ uint4 split_x(const uint4 a, const uint4 b) {
+  const auto sx = __builtin_amdgcn_permlane32_swap(a.x, b.x, false, false);
+  const auto sy = __builtin_amdgcn_permlane32_swap(a.y, b.y, false, false);
+  const auto sz = __builtin_amdgcn_permlane32_swap(a.z, b.z, false, false);
+  const auto sw = __builtin_amdgcn_permlane32_swap(a.w, b.w, false, false);
+  return make_uint4((uint32_t)sx[H], (uint32_t)sy[H], (uint32_t)sz[H], (uint32_t)sw[H]);
+}
+
+// Table of one half for one batch row into buffer `buf`: lane l builds chunk
+// l & 31 for the row of its half-wave (the low word of each pair for lanes
+// 0-31, the high word for 32-63), the 16 entries whose high nibble is the
+// wave index, in Gray-code order as in build_table.
+__device__ __forceinline__ void build_split(float* lut, int buf, const LaneCtx& l, const uint4 xr) {
+  float x[8];
+  unpack8(xr, x);
+  const int h0 = l.wave;
+  const float c = ((h0 & 1) ? x[4] : -x[4]) + ((h0 & 2) ? x[5] : -x[5]);
+  const float d = ((h0 & 4) ? x[6] : -x[6]) + ((h0 & 8) ? x[7] : -x[7]);
+  float T = (-(x[0] + x[1]) - (x[2] + x[3])) + (c + d);
+  float two[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) two[t] = x[t] + x[t];
+  float* base = reinterpret_cast<float*>(reinterpret_cast<char*>(lut) + buf * (kLutWords * 4) +
+                                         h0 * 16 * 256 + (l.lane & 31) * 8 + (l.lane >> 5) * 4);
+  base[0] = T;
+#pragma unroll
+  for (int n = 1; n < 16; ++n) {
+    const int t = __builtin_ctz(n);
+    const int pat = n ^ (n >> 1);
+    T += ((pat >> t) & 1) ? two[t] : -two[t];
+    base[pat * 64] = T;
+  }
+}
+
+// Lookups of half H of batch rows 2h and 2h+1 (T arranged by split_arrange;
+// the table of half H is in buffer H). acc[r][j]: batch row r, row
+// 4*r4 + 2*rh + j of the lane's row tile.
+template <int Q, int MC, bool OFF, int H>
+__device__ __forceinline__ void lookups_split(const LaneCtx& l, int h, const float* lut,
+                                              const TileRegs<Q, 1, MC, true, OFF>& T,
+                                              float (&acc)[MC][2]) {
+  const int r0 = 2 * h, r1 = 2 * h + 1;
+  uint32_t hs[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) hs[k] = l.hsel[k] | ((uint32_t)H << 16);
+  float cs0 = 0.f, cs1 = 0.f;
+  if constexpr (OFF) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 e = lut_at2(lut, (0xFFu << 8) | hs[k]);
+      cs0 = k == 0 ? e.x : cs0 + e.x;
+      cs1 = k == 0 ? e.y : cs1 + e.y;
+    }
+  }
+  if (T.pos.c.valid_rpw > 0) {  // uniform over the wave
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const uint32_t words[2] = {H ? T.bw[0][q].z : T.bw[0][q].x,
+                                 H ? T.bw[0][q].w : T.bw[0][q].y};
+      float2 e[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          e[j][k] = lut_at2(lut, __builtin_amdgcn_perm(words[j], hs[k], l.psel[k]));
+      const uint32_t aword = T.aw[0][2 * q + H];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float s0 = (e[j][0].x + e[j][1].x) + (e[j][2].x + e[j][3].x);
+        const float s1 = (e[j][0].y + e[j][1].y) + (e[j][2].y + e[j][3].y);
+        const float al = h2f(aword, j);
+        acc[r0][j] = __builtin_fmaf(al, s0, acc[r0][j]);
+        acc[r1][j] = __builtin_fmaf(al, s1, acc[r1][j]);
+      }
+    }
+    if constexpr (OFF) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float o = h2f(T.ow[0][H], j);
+        acc[r0][j] = __builtin_fmaf(o, cs0, acc[r0][j]);
+        acc[r1][j] = __builtin_fmaf(o, cs1, acc[r1][j]);
+      }
+    }
+  }
+}
+
+// Sum a lane's two row accumulators over the 8 lanes of its row pair (bits
+// 0-2 of the lane) with DPP moves, as the last three steps of row_sum16: the
+// sum of row j = lane & 1 ends in the lanes with (lane & 6) == 4.
+__device__ __forceinline__ float row_sum8(const float (&v)[2], int lane) {
+  const bool odd = (lane & 1) != 0;
+  const float keep = odd ? v[1] : v[0];
+  const float send = odd ? v[0] : v[1];
+  float t = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                                 __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+  t += __builtin_bit_cast(float,
+                          __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x4E, 0xF, 0xF, false));
+  t += __builtin_bit_cast(float,
+                          __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x114, 0xF, 0xF, false));
+  return t;
+}
+
+// finish_item for the split paired tables: reduce, store, clear.
+template <int MC>
+__device__ __forceinline__ void finish_split(const Params& p, const LaneCtx& l, const ItemCtx& c,
+                                             float (&acc)[MC][2]) {
+  const bool split_mode = p.S > 1;
+#pragma unroll
+  for (int r = 0; r < MC; ++r) {
+    if (r < c.rows_here && c.valid_rpw > 0) {
+      const float v[2] = {acc[r][0], acc[r][1]};
+      const float t = row_sum8(v, l.lane);
+      const int row = c.rt_first * kRowTile + 4 * l.r4 + 2 * (l.lane >> 5) + (l.lane & 1);
+      if (holds_row_sum(l.lane)) {
+        if (split_mode) {
+          __hip_atomic_store(&p.partial[((size_t)c.split * p.m + (c.r0 + r)) * p.Npad + row], t,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (row < p.N) {
+          p.y[(size_t)(c.r0 + r) * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)t);
+        }
+      }
+    }
+    acc[r][0] = 0.f;
+    acc[r][1] = 0.f;
+  }
+}
+
 // Reduce the accumulators of a finished item over the 16 lanes that share a
 // row quad (row_sum16), store them (fp16 y, or this split's fp32 partials)
 // and clear them.
@@ -851,8 +1019,12 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // HT (with PR): half paired tables in two buffers; each step (one pair of
 // batch rows of one tile) looks up one buffer, builds the next step's table in
 // the other and ends at the step's one barrier.
+// SP (with PR, 16 waves, one row tile per wave): split paired tables; each
+// tile takes two steps per pair of batch rows, one per half of its chunks,
+// each looking up one buffer, building the next step's table in the other and
+// ending at its one barrier.
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL, bool PR = false,
-          bool EI = false, bool ONCE = false, bool HT = false>
+          bool EI = false, bool ONCE = false, bool HT = false, bool SP = false>
 // The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
 // also the most that can ever run; saying so lets the scheduler use the
 // whole register budget to keep table lookups in flight.
@@ -863,6 +1035,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   static_assert(!EI || (XL && NR == 2 && !PR), "early issue: x in LDS, two register sets");
   static_assert(!ONCE || (!XL && !PR && MC == 1), "read-once loads: batch 1 without x in LDS");
   static_assert(!HT || PR, "half tables are paired");
+  static_assert(!SP || (PR && !HT && RPW == 1 && W == 16), "split paired tables: 16 waves x 1 row tile");
   __shared__ float lut[2 * kLutWords];
   __shared__ uint4 xs[XL ? kXChunks : 1];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
@@ -934,7 +1107,47 @@ __global__ void __launch_bounds__(W * 64, W / 4)
       return T.xv[r];
     }
   };
-  if constexpr (HT) {
+  if constexpr (SP) {
+    float sacc[MC][2];
+#pragma unroll
+    for (int r = 0; r < MC; ++r) sacc[r][0] = sacc[r][1] = 0.f;
+    build_split(lut, 0, l, split_x<0>(R[0].xv[0], R[0].xv[1]));
+    __syncthreads();
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        if (!done) {
+          TR& cur = R[s];
+          TR& nxt = R[(s + 1) % NR];
+          TR& pre = R[(s + NR - 1) % NR];
+          pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
+          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
+          split_arrange<Q, MC, OFF>(cur);
+#pragma unroll
+          for (int h = 0; h < MC / 2; ++h) {
+            if (2 * h < cur.pos.c.rows_here) {  // uniform over the workgroup
+              lookups_split<Q, MC, OFF, 0>(l, h, lut, cur, sacc);
+              build_split(lut, 1, l, split_x<1>(cur.xv[2 * h], cur.xv[2 * h + 1]));
+              __syncthreads();
+              lookups_split<Q, MC, OFF, 1>(l, h, lut, cur, sacc);
+              const int hn = 2 * h + 2 < MC ? 2 * h + 2 : 0;   // a constant once unrolled
+              if (2 * h + 2 < cur.pos.c.rows_here) {
+                build_split(lut, 0, l, split_x<0>(cur.xv[hn], cur.xv[hn + 1]));
+              } else if (nxt.pos.live) {
+                build_split(lut, 0, l, split_x<0>(nxt.xv[0], nxt.xv[1]));
+              }
+              __syncthreads();
+            }
+          }
+          if (cur.pos.kt + 1 == cur.pos.c.kt1) finish_split<MC>(p, l, cur.pos.c, sacc);
+          done = !nxt.pos.live;
+        }
+      }
+    }
+    if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    return;
+  } else if constexpr (HT) {
     int buf = 0;
     build_half_pair<W>(lut, 0, l, R[0].xv[0], R[0].xv[1]);
     __syncthreads();
@@ -1395,12 +1608,21 @@ constexpr int kRingPair =
 // tables (grouped scales, even MC); ei the early-issue ring of the x-in-LDS
 // variant (default ring only); once the read-once (non-temporal) sign-plane
 // loads of the 16-wave batch-1 instances without x in LDS.
-// pr: 1 paired tables, 2 half paired tables (one row tile per wave only).
+// pr: 1 paired tables, 2 half paired tables (one row tile per wave only), 3
+// split paired tables (16 waves, one row tile per wave, two batch rows).
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
 KernelFn kernel_or_null(int ring, bool xl, int pr, bool ei, bool once) {
   if (pr) {
     if constexpr (GQ && kRingPair<Q, RPW, MC, OFF, W> > 0) {
       if (xl) return nullptr;
+      if (pr == 3) {
+        if constexpr (RPW == 1 && W == 16 && MC == 2) {
+          return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true,
+                                false, false, false, true>;
+        } else {
+          return nullptr;
+        }
+      }
       if (pr == 2) {
         if constexpr (RPW == 1) {
           return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true,
@@ -1475,7 +1697,7 @@ KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, int 
 // The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
 // item, scale groups aligned to 32 inputs (gq), an offset term (off), w waves
 // per workgroup, ring depth (0 default, >= 3 deeper), x in LDS (xl), paired
-// tables (pr: 1 paired, 2 half paired), the early-issue ring (ei) and read-once
+// tables (pr: 1 paired, 2 half paired, 3 split paired), the early-issue ring (ei) and read-once
 // sign-plane loads (once), or nullptr if none is built.
 template <int Q>
 KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, int pr,
