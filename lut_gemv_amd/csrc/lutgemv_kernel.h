@@ -1439,6 +1439,15 @@ __global__ void __launch_bounds__(1024, 4) __attribute__((amdgpu_waves_per_eu(4,
 #pragma unroll
     for (int j = 0; j < NX; ++j)
       xr[j] = load16(xrs, ((uint32_t)threadIdx.x + (uint32_t)(j * 1024)) * 16u);
+    // x reaches LDS before the weight loads are issued: issued behind the
+    // first NR tiles of every workgroup, its loads would wait in the memory
+    // queues behind all of them (measured 5-6% faster on 28672 x 8192 and
+    // 512 x 512)
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const int c = (int)threadIdx.x + j * 1024;
+      if (c < nchunks) xs[c] = xr[j];
+    }
     asm volatile("" ::: "memory");
   }
   const UnitPlan<Q, UPW> P = unit_plan<Q, UPW>(p, l, rt0, nunits);
@@ -1448,11 +1457,6 @@ __global__ void __launch_bounds__(1024, 4) __attribute__((amdgpu_waves_per_eu(4,
   if (has_units) {
 #pragma unroll
     for (int s = 0; s < NR; ++s) load_units<Q, OFF, UPW>(p, l, P, ic, R[s]);
-  }
-#pragma unroll
-  for (int j = 0; j < NX; ++j) {
-    const int c = (int)threadIdx.x + j * 1024;
-    if (c < nchunks) xs[c] = xr[j];
   }
   __syncthreads();
   build_nibbles(lut, xs, 0, nchunks);
