@@ -69,7 +69,8 @@ typedef enum lutgemm_status {
   LUTGEMM_ERR_ALIGN = 5,       /* a device pointer is not aligned as required        */
   LUTGEMM_ERR_UNSUPPORTED = 6, /* the current device is not gfx950 (the environment  */
                                /* variable LUTGEMM_FAKE_ARCH, a debugging aid,      */
-                               /* replaces the name the device reports)             */
+                               /* replaces the name the device reports), or the     */
+                               /* call needs a feature this build lacks             */
   LUTGEMM_ERR_HIP = 7,         /* a HIP runtime call or a kernel launch failed       */
   LUTGEMM_ERR_INTERNAL = 8     /* unexpected internal failure                        */
 } lutgemm_status;
@@ -244,6 +245,21 @@ typedef struct lutgemm_plan {
 } lutgemm_plan;
 int lutgemm_query_plan(const lutgemm_shape* s, int32_t m, int32_t cus, size_t workspace_bytes,
                        lutgemm_plan* out);
+
+/* Phase timestamps, a tracing aid. In the library built with phase tracing
+ * (liblutgemm_trace.so, built beside liblutgemm.so from the same sources),
+ * every launch of the GEMV kernels that starts after this call writes, for
+ * each workgroup w below bytes / 64, stamps of the GPU's constant 100 MHz clock
+ * into the device buffer d_buffer as uint64 [w][8]: index 0 at the
+ * workgroup's start, 1 when x is staged in LDS (batch 1), 2 when the first
+ * table is built, 3 when the first step is done, 4 when its last lookups are
+ * done, 5 at its end; a launch leaves the indices it does not pass as they
+ * were. Results are those of the regular library. NULL detaches. The buffer
+ * belongs to the caller and must stay valid while traced launches run;
+ * launches that overlap in time write the same buffer.
+ * Errors: ALIGN when d_buffer is not 8-byte aligned; the regular library
+ * returns UNSUPPORTED and records nothing. Host only (no HIP call). */
+int lutgemm_trace_attach(void* d_buffer, size_t bytes);
 
 /* Storage in bits of the matrix of shape *s: q sign bits per weight, one fp16
  * scale per (plane, row, group of g) and one fp16 offset per (row, group) when

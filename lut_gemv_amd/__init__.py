@@ -22,11 +22,13 @@ __all__ = [
     "check_shape", "packed_sizes", "workspace_size", "workspace_init",
     "bcq_pack", "bcq_pack_uniform", "lutgemm_run", "bcq_dequant_gemv", "footprint_bits",
     "search_group_sizes", "bcq_quantize", "stream_read", "lutgemm_run_noalloc",
-    "noalloc_scratch_bytes", "query_plan", "TABLES", "PackedBCQ", "STATUS",
+    "noalloc_scratch_bytes", "query_plan", "TABLES", "trace_attach", "use_traced_library",
+    "PackedBCQ", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblutgemm.so")
+TRACE_LIB_PATH = os.path.join(_HERE, "liblutgemm_trace.so")
 
 STATUS = {
     0: "LUTGEMM_OK", 1: "LUTGEMM_ERR_NULL", 2: "LUTGEMM_ERR_SHAPE", 3: "LUTGEMM_ERR_VALUE",
@@ -116,6 +118,8 @@ def lib() -> ctypes.CDLL:
     L.lutgemm_noalloc_scratch_bytes.argtypes = []
     L.lutgemm_stream_read.restype = ctypes.c_int
     L.lutgemm_stream_read.argtypes = [_P, _SZ, _P, _SZ, ctypes.c_int, _P]
+    L.lutgemm_trace_attach.restype = ctypes.c_int
+    L.lutgemm_trace_attach.argtypes = [_P, _SZ]
     L.lutgemm_query_plan.restype = ctypes.c_int
     L.lutgemm_query_plan.argtypes = [_SHP, ctypes.c_int32, ctypes.c_int32, _SZ,
                                      ctypes.POINTER(_Plan)]
@@ -262,6 +266,21 @@ def query_plan(N: int, K: int, q: int, g: int, has_offset: bool, m: int, cus: in
     d = {f: int(getattr(pl, f)) for f, _ in _Plan._fields_ if f != "reserved"}
     d["tables"] = TABLES[d["tables"]]
     return d
+
+
+def use_traced_library() -> None:
+    """Make this process load the phase-traced build (liblutgemm_trace.so)
+    instead of the regular one; call before anything else of this module."""
+    global LIB_PATH
+    if _LIB is not None and LIB_PATH != TRACE_LIB_PATH:
+        raise RuntimeError("the regular library is already loaded in this process")
+    LIB_PATH = TRACE_LIB_PATH
+
+
+def trace_attach(d_buffer: Optional[int], nbytes: int) -> None:
+    """Phase stamps of later launches into a device buffer of uint64
+    [workgroup][8] (lutgemm_trace_attach); the traced library only."""
+    _check(lib().lutgemm_trace_attach(d_buffer, int(nbytes)), "lutgemm_trace_attach")
 
 
 def footprint_bits(N: int, K: int, q: int, g: int, has_offset: bool = False) -> int:

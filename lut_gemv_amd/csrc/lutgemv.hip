@@ -390,6 +390,10 @@ int device_scratch(int dev, hipStream_t strm, void** out) {
 // Enqueue the product for a validated shape and configuration (K > 0): the
 // kernel instance, its parameters and its persistent grid of min(items, cus)
 // workgroups. `ws` is the workspace of a split launch (counters, then partials).
+// Phase-trace buffer (traced builds only; see lutgemm_trace_attach).
+std::atomic<unsigned long long*> g_trace{nullptr};
+std::atomic<int64_t> g_trace_wgs{0};
+
 int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d_bits,
            const void* d_alpha, const void* d_offset, const void* d_x, void* d_y, void* ws,
            hipStream_t strm) {
@@ -398,6 +402,8 @@ int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d
                                    c.pr, c.ei, c.once);
   if (!fn) return LUTGEMM_ERR_INTERNAL;
   Params p{};
+  p.trace = g_trace.load(std::memory_order_relaxed);
+  p.trace_wgs = (int)g_trace_wgs.load(std::memory_order_relaxed);
   p.bits = (const uint8_t*)d_bits;
   p.alpha = (const uint32_t*)d_alpha;
   p.offset = G.has_offset ? (const uint32_t*)d_offset : nullptr;
@@ -540,6 +546,21 @@ int lutgemm_run(const lutgemm_shape* s, int32_t m, const void* d_bits, const voi
   } catch (...) {
     return LUTGEMM_ERR_INTERNAL;
   }
+}
+
+int lutgemm_trace_attach(void* d_buffer, size_t bytes) {
+#ifdef LUTGEMM_PHASE_TRACE
+  if (d_buffer && ((uintptr_t)d_buffer & 7)) return LUTGEMM_ERR_ALIGN;
+  const size_t per_wg = (size_t)kTracePoints * sizeof(unsigned long long);
+  const size_t wgs = d_buffer ? bytes / per_wg : 0;
+  g_trace_wgs.store((int64_t)(wgs < 0x7FFFFFFF ? wgs : 0x7FFFFFFF), std::memory_order_relaxed);
+  g_trace.store(d_buffer ? (unsigned long long*)d_buffer : nullptr, std::memory_order_relaxed);
+  return LUTGEMM_OK;
+#else
+  (void)d_buffer;
+  (void)bytes;
+  return LUTGEMM_ERR_UNSUPPORTED;
+#endif
 }
 
 int lutgemm_query_plan(const lutgemm_shape* s, int32_t m, int32_t cus, size_t workspace_bytes,

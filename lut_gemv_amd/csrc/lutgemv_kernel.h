@@ -82,7 +82,41 @@ struct Params {
   int g_span;               // most scale groups one input tile touches
   int g_tile;               // 1 if g divides 512: every input tile starts a group
   int xcd_bg;               // 1: the batch groups of one weight block are 8 items apart
+  unsigned long long* trace;   // phase stamps [workgroup][kTracePoints] (traced builds only)
+  int trace_wgs;               // workgroups the trace buffer holds
 };
+
+// Phase tracing (a tracing aid, compiled in only with LUTGEMM_PHASE_TRACE):
+// thread 0 of each workgroup stamps the GPU's constant 100 MHz clock at the
+// phase boundaries of a launch: 0 start, 1 x staged in LDS, 2 first table
+// built, 3 first step done, 4 last lookups done, 5 end. In the regular build
+// the macros are empty and the two fields above stay null.
+constexpr int kTracePoints = 8;
+#ifdef LUTGEMM_PHASE_TRACE
+#define LUTGEMM_PHASE(k)                                                                   \
+  do {                                                                                     \
+    if (p.trace && threadIdx.x == 0 && (int)blockIdx.x < p.trace_wgs)                       \
+      p.trace[(size_t)blockIdx.x * kTracePoints + (k)] = __builtin_amdgcn_s_memrealtime();  \
+  } while (0)
+#define LUTGEMM_PHASE_FLAG(f) bool f = false
+#define LUTGEMM_PHASE_ONCE(k, f) \
+  do {                           \
+    if (!(f)) {                  \
+      (f) = true;                \
+      LUTGEMM_PHASE(k);          \
+    }                            \
+  } while (0)
+#else
+#define LUTGEMM_PHASE(k) \
+  do {                   \
+  } while (0)
+#define LUTGEMM_PHASE_FLAG(f) \
+  do {                        \
+  } while (0)
+#define LUTGEMM_PHASE_ONCE(k, f) \
+  do {                           \
+  } while (0)
+#endif
 
 __device__ __forceinline__ float h2f(uint32_t word, int hi) {
   const uint16_t bitsv = hi ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
@@ -1036,6 +1070,9 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   static_assert(!ONCE || (!XL && !PR && MC == 1), "read-once loads: batch 1 without x in LDS");
   static_assert(!HT || PR, "half tables are paired");
   static_assert(!SP || (PR && !HT && RPW == 1 && W == 16), "split paired tables: 16 waves x 1 row tile");
+  LUTGEMM_PHASE(0);
+  LUTGEMM_PHASE_FLAG(traced_table);
+  LUTGEMM_PHASE_FLAG(traced_step);
   __shared__ float lut[2 * kLutWords];
   __shared__ uint4 xs[XL ? kXChunks : 1];
   using TR = TileRegs<Q, RPW, MC, GQ, OFF>;
@@ -1098,6 +1135,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
       if (c < nchunks) xs[c] = xr[j];
     }
     __syncthreads();
+    LUTGEMM_PHASE(1);
   }
   // activations of chunk `lane` of a tile, for the table build
   auto xtile = [&](const TR& T, int r) -> uint4 {
@@ -1113,6 +1151,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     for (int r = 0; r < MC; ++r) sacc[r][0] = sacc[r][1] = 0.f;
     build_split(lut, 0, l, split_x<0>(R[0].xv[0], R[0].xv[1]));
     __syncthreads();
+    LUTGEMM_PHASE(2);
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -1138,6 +1177,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
                 build_split(lut, 0, l, split_x<0>(nxt.xv[0], nxt.xv[1]));
               }
               __syncthreads();
+              LUTGEMM_PHASE_ONCE(3, traced_step);
             }
           }
           if (cur.pos.kt + 1 == cur.pos.c.kt1) finish_split<MC>(p, l, cur.pos.c, sacc);
@@ -1145,12 +1185,15 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         }
       }
     }
+    LUTGEMM_PHASE(4);
     if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    LUTGEMM_PHASE(5);
     return;
   } else if constexpr (HT) {
     int buf = 0;
     build_half_pair<W>(lut, 0, l, R[0].xv[0], R[0].xv[1]);
     __syncthreads();
+    LUTGEMM_PHASE(2);
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -1172,6 +1215,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
                 build_half_pair<W>(lut, buf ^ 1, l, nxt.xv[0], nxt.xv[1]);
               }
               __syncthreads();
+              LUTGEMM_PHASE_ONCE(3, traced_step);
               buf ^= 1;
             }
           }
@@ -1180,7 +1224,9 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         }
       }
     }
+    LUTGEMM_PHASE(4);
     if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    LUTGEMM_PHASE(5);
     return;
   } else if constexpr (PR) {
     bool done = false;
@@ -1199,20 +1245,25 @@ __global__ void __launch_bounds__(W * 64, W / 4)
               __syncthreads();                  // the previous lookups are done
               build_table_pair<W>(lut, l, cur.xv[2 * h], cur.xv[2 * h + 1]);
               __syncthreads();
+              LUTGEMM_PHASE_ONCE(2, traced_table);
               lookups_pair<Q, RPW, MC, OFF>(l, h, lut, cur, acc);
             }
           }
+          LUTGEMM_PHASE_ONCE(3, traced_step);
           if (cur.pos.kt + 1 == cur.pos.c.kt1) finish_item<RPW, MC>(p, l, cur.pos.c, acc);
           done = !nxt.pos.live;
         }
       }
     }
+    LUTGEMM_PHASE(4);
     if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    LUTGEMM_PHASE(5);
     return;
   }
   int buf = 0;
   build_table<W>(lut, 0, l, xtile(R[0], 0));
   __syncthreads();
+  LUTGEMM_PHASE(2);
   if constexpr (EI) {
     for (;;) {
 #pragma unroll
@@ -1226,13 +1277,16 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         if (was.live) {
           if (nxt.pos.live) build_table<W>(lut, buf ^ 1, l, xtile(nxt, 0));
           __syncthreads();
+          LUTGEMM_PHASE_ONCE(3, traced_step);
           buf ^= 1;
           if (was.kt + 1 == was.c.kt1) finish_item<RPW, MC>(p, l, was.c, acc);
         }
       }
       if (!R[0].pos.live) break;
     }
+    LUTGEMM_PHASE(4);
     if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+    LUTGEMM_PHASE(5);
     return;
   }
   bool done = false;
@@ -1255,6 +1309,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
               build_table<W>(lut, buf ^ 1, l, xtile(nxt, 0));
             }
             __syncthreads();
+            LUTGEMM_PHASE_ONCE(3, traced_step);
             buf ^= 1;
           }
         }
@@ -1263,7 +1318,9 @@ __global__ void __launch_bounds__(W * 64, W / 4)
       }
     }
   }
+  LUTGEMM_PHASE(4);
   if (p.S > 1) split_epilogue<RPW, MC, W>(p, reinterpret_cast<int*>(lut));
+  LUTGEMM_PHASE(5);
 }
 
 // ------------------------------------------------------------------ unit kernel
@@ -1423,6 +1480,8 @@ template <int Q, bool OFF, int UPW, int NR>
 __global__ void __launch_bounds__(1024, 4) __attribute__((amdgpu_waves_per_eu(4, 4)))
     lutgemv_nibble_kernel(Params p) {
   static_assert(kPhaseTiles % NR == 0, "the ring depth divides the tiles of a phase");
+  LUTGEMM_PHASE(0);
+  LUTGEMM_PHASE_FLAG(traced_step);
   __shared__ float lut[2 * 16 * kPhaseChunks];
   __shared__ uint4 xs[kXChunks];
   LaneCtx l = lane_ctx();
@@ -1459,8 +1518,10 @@ __global__ void __launch_bounds__(1024, 4) __attribute__((amdgpu_waves_per_eu(4,
     for (int s = 0; s < NR; ++s) load_units<Q, OFF, UPW>(p, l, P, ic, R[s]);
   }
   __syncthreads();
+  LUTGEMM_PHASE(1);
   build_nibbles(lut, xs, 0, nchunks);
   __syncthreads();
+  LUTGEMM_PHASE(2);
 
   // per visit k and half j: the rotation that brings the half's nibble of byte
   // b_k to bits 13-16, and the table base (half, chunk 4*c4 + b_k of the tile)
@@ -1538,8 +1599,10 @@ __global__ void __launch_bounds__(1024, 4) __attribute__((amdgpu_waves_per_eu(4,
         }
       }
       load_units<Q, OFF, UPW>(p, l, P, ic, cur);
+      LUTGEMM_PHASE_ONCE(3, traced_step);       // wave 0's first tile
     }
   }
+  LUTGEMM_PHASE(4);
   __syncthreads();                              // every lookup done: the tables are free
   float* red = lut;
 #pragma unroll
@@ -1560,6 +1623,7 @@ __global__ void __launch_bounds__(1024, 4) __attribute__((amdgpu_waves_per_eu(4,
     const int n = (rt0 + rtl) * kRowTile + row;
     if (n < p.N) p.y[n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
   }
+  LUTGEMM_PHASE(5);
 }
 
 // ------------------------------------------------------------------ instances

@@ -83,7 +83,7 @@ const char* lutgemm_status_string(int status) {
     case LUTGEMM_ERR_VALUE: return "invalid value (code or zero-point out of range, non-finite or overflowing scale)";
     case LUTGEMM_ERR_BUFFER: return "buffer or workspace too small";
     case LUTGEMM_ERR_ALIGN: return "device pointer misaligned";
-    case LUTGEMM_ERR_UNSUPPORTED: return "unsupported device (gfx950 required)";
+    case LUTGEMM_ERR_UNSUPPORTED: return "unsupported device (gfx950 required) or feature not in this build";
     case LUTGEMM_ERR_HIP: return "HIP runtime error";
     case LUTGEMM_ERR_INTERNAL: return "internal error";
     default: return "unknown status";

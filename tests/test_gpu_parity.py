@@ -536,6 +536,56 @@ def test_stream_read_probe_runs():
         lg.stream_read(src.data_ptr() + 8, n - 16, sink.data_ptr(), sink.numel(), True, sh)
 
 
+# the phase-traced build: same results as the regular one, stamps in order
+@pytest.mark.parametrize("N,K,q,g,m,off,tile", [
+    (32768, 4096, 3, 128, 1, False, None),   # x in LDS, early-issue ring (8 row tiles per CU)
+    (4096, 12288, 3, 128, 1, True, None),    # split of the input dimension
+    (4096, 4096, 2, 128, 1, False, None),    # nibble tables
+    (2048, 3072, 3, 64, 4, True, "1,2,16,2,0,16,0,1"),   # paired tables
+])
+def test_phase_traced_build(monkeypatch, N, K, q, g, m, off, tile):
+    import ctypes
+    if not os.path.exists(lg.TRACE_LIB_PATH):
+        pytest.skip("phase-traced library not built")
+    if tile:
+        monkeypatch.setenv("LUTGEMM_TILE", tile)
+    T = ctypes.CDLL(lg.TRACE_LIB_PATH)
+    T.lutgemm_trace_attach.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    T.lutgemm_run.argtypes = [ctypes.POINTER(lg.Shape), ctypes.c_int32] + [ctypes.c_void_p] * 6 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + K + m, with_offset=off, name=f"trace_{N}x{K}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    x = torch.from_numpy(w.x).to(DEV)
+    y_ref = pw(x)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = lg.query_plan(N, K, q, g, off, m, cus=cus,
+                         workspace_bytes=None if cus == 256 else lg.workspace_size(N, K, q, g, off, m))
+    _say(f"phase-traced build: {N}x{K} q={q} g={g} m={m} offset={off} plan={plan}")
+    nwg = plan["workgroups"]
+    stamps = torch.zeros(nwg * 8, dtype=torch.int64, device=DEV)
+    nws = max(16, lg.workspace_size(N, K, q, g, off, m))
+    wsp = torch.zeros(nws, dtype=torch.uint8, device=DEV)
+    y = torch.empty((m, N), dtype=torch.float16, device=DEV)
+    sh = torch.cuda.current_stream().cuda_stream
+    assert T.lutgemm_trace_attach(stamps.data_ptr(), stamps.numel() * 8) == 0
+    try:
+        for _ in range(2):
+            st = T.lutgemm_run(ctypes.byref(pw.shape), m, pw.d_bits.data_ptr(), pw.d_alpha.data_ptr(),
+                               pw.d_offset.data_ptr() if pw.has_offset else None, x.data_ptr(),
+                               y.data_ptr(), wsp.data_ptr(), nws, sh)
+            assert st == 0
+        torch.cuda.synchronize()
+    finally:
+        T.lutgemm_trace_attach(None, 0)
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    t = stamps.cpu().numpy().reshape(nwg, 8)
+    assert (t[:, 0] > 0).all() and (t[:, 5] > 0).all() and (t[:, 6:] == 0).all()
+    order = [0, 2, 3, 4, 5]
+    for a, b in zip(order, order[1:]):
+        assert (t[:, b] >= t[:, a]).all(), (a, b)
+    assert ((t[:, 5] - t[:, 0]) < 100_000).all()    # under 1 ms at 100 MHz
+
+
 # the nibble-table unit kernel (batch 1, few row tiles per compute unit):
 # "0,1,16,1,NR,RI,1,0,0,1" forces it with RI row tiles per workgroup and ring depth NR
 @pytest.mark.parametrize("N,K,q,g,off,ri,nr", [

@@ -36,6 +36,31 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
+def _load_traced():
+    if not os.path.exists(lg.TRACE_LIB_PATH):
+        pytest.skip("phase-traced library not built")
+    import torch  # noqa: F401  (the HIP runtime first, as the binding does)
+    L = ctypes.CDLL(lg.TRACE_LIB_PATH)
+    L.lutgemm_trace_attach.restype = ctypes.c_int
+    L.lutgemm_trace_attach.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    return L
+
+
+def test_phase_trace_entry_point():
+    """The regular library refuses phase tracing; the traced build, built from
+    the same sources, exports the same symbols and checks the buffer."""
+    assert lg.lib().lutgemm_trace_attach(None, 0) == 6
+    assert lg.lib().lutgemm_trace_attach(0x1000, 4096) == 6
+    L = _load_traced()
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", lg.TRACE_LIB_PATH], capture_output=True,
+                         text=True).stdout
+    assert set(_declared_functions()) <= set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    assert L.lutgemm_trace_attach(0x1004, 4096) == 5       # not 8-byte aligned
+    assert L.lutgemm_trace_attach(0x1000, 4096) == 0       # host only: nothing is touched
+    assert L.lutgemm_trace_attach(None, 0) == 0            # detached again
+
+
 def test_abi_version_and_status_strings():
     assert lg.abi_version() == 1
     for st in range(9):
