@@ -1043,8 +1043,8 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // barrier and the pair's lookups.
 // EI (with XL and two register sets): a set is refilled with the tile two
 // ahead as soon as its lookups are done, instead of at the start of the next
-// step, so two tiles are in flight from the start (the staging of x and the
-// first table build overlap both). That loop leaves only after its second
+// step, so two tiles are in flight from the start (the first table build
+// overlaps both, the staging of x the first). That loop leaves only after its second
 // step and issues its loads unconditionally: every path into the loop head
 // then has the same loads outstanding, and the compiler's wait counts before
 // the lookups stay exact (they would otherwise also wait for the tile ahead).
@@ -1118,10 +1118,6 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     asm volatile("" ::: "memory");
     if (!R[0].pos.live) return;
   }
-  if constexpr (EI) {
-    R[1].pos = next_tile<RPW, MC, W>(p, l.wave, R[0].pos);
-    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[1]);
-  }
 #pragma unroll
   for (int s = 1; s + 1 < NR; ++s) {
     R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
@@ -1136,6 +1132,14 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     }
     __syncthreads();
     LUTGEMM_PHASE(1);
+  }
+  // EI: the second tile's loads go out once x is staged, not with the first
+  // tile's: a wave held at issuing them (the CU's memory queue is full at the
+  // start) then no longer delays the barrier above (x staged at 1.9 instead of
+  // 3.6 us on 49152 x 12288; 0.3-1% faster on 32768-65536 rows).
+  if constexpr (EI) {
+    R[1].pos = next_tile<RPW, MC, W>(p, l.wave, R[0].pos);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[1]);
   }
   // activations of chunk `lane` of a tile, for the table build
   auto xtile = [&](const TR& T, int r) -> uint4 {
