@@ -219,7 +219,10 @@ size_t lutgemm_noalloc_scratch_bytes(void);
  *   LUTGEMM_TABLES_NIBBLE  16-entry tables of 4-input halves of each chunk,
  *                          a byte's entry being the sum of its two halves';
  *   LUTGEMM_TABLES_SPLIT   paired tables built for half an input tile at a
- *                          time (32 chunks), two buffers.
+ *                          time (32 chunks), two buffers;
+ *   LUTGEMM_TABLES_PAIRED_MFMA  paired tables whose entries are computed by
+ *                          matrix-core instructions (the 256 x 8 sign matrix
+ *                          times the tile's activations).
  * Fields of a plan with no launch (m == 0, N == 0 or K == 0) are zero.
  * Errors: NULL when s or out is NULL, SHAPE as for lutgemm_run or when
  * cus < 1, INTERNAL when no kernel instance fits. */
@@ -228,7 +231,8 @@ enum {
   LUTGEMM_TABLES_PAIRED = 1,
   LUTGEMM_TABLES_HALF = 2,
   LUTGEMM_TABLES_NIBBLE = 3,
-  LUTGEMM_TABLES_SPLIT = 4
+  LUTGEMM_TABLES_SPLIT = 4,
+  LUTGEMM_TABLES_PAIRED_MFMA = 5
 };
 typedef struct lutgemm_plan {
   int32_t tables;         /* LUTGEMM_TABLES_*                                   */

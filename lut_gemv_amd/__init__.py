@@ -44,7 +44,7 @@ class LutGemmError(RuntimeError):
         super().__init__(f"{where}: {self.name} ({status_string(status)})")
 
 
-TABLES = {0: "single", 1: "paired", 2: "half", 3: "nibble", 4: "split"}
+TABLES = {0: "single", 1: "paired", 2: "half", 3: "nibble", 4: "split", 5: "paired_mfma"}
 
 
 class _Plan(ctypes.Structure):

@@ -84,7 +84,7 @@ struct Config {
   bool xl;               // x staged in LDS
   int pr;                // 1: paired tables (two batch rows per table entry), 2: half
                          // paired tables, 3: split paired tables (both double-buffered),
-                         // 0: neither
+                         // 4: paired tables built by MFMA, 0: none of these
   bool ei;               // early-issue ring (x in LDS, two register sets)
   bool once;             // batch 1 without x in LDS: non-temporal sign-plane loads
   bool us;               // the nibble-table unit kernel (batch 1, few row tiles per CU)
@@ -107,8 +107,8 @@ struct TileOverride {
 // Optional tuning override "RPW,S[,W[,MC[,ring[,RI[,XL[,PR[,EI[,US]]]]]]]]" (LUTGEMM_TILE);
 // never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
 // (default: where possible). PR: 1 paired tables, 2 half paired tables, 3
-// split paired tables, each where an instance has them, 0 never (default: the
-// dispatcher's choice). EI: 1 the early-issue ring where
+// split paired tables, 4 paired tables built by MFMA, each where an instance
+// has them, 0 never (default: the dispatcher's choice). EI: 1 the early-issue ring where
 // x is staged in LDS with the default ring, 0 never (the default). US: 1 the
 // nibble-table unit kernel where it applies (batch 1, scale groups dividing or
 // multiples of 512 inputs, x in LDS) with RI row tiles per workgroup (default:
@@ -206,11 +206,13 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
     // this model picks they measured 9-27% faster than 16 waves x 1 row at
     // m = 2..10 (12288 x 12288: 24.9 -> 22.2 us at m = 2, 39.5 -> 34.6 at 4,
     // 68.3 -> 53.8 at 8; 49152 x 12288 at m = 4: 130.2 -> 103.1), the same at
-    // m = 16, and the model keeps 16 x 1 at odd m = 3, 5.
+    // m = 16, and the model keeps 16 x 1 at odd m = 3, 5. Their tables are
+    // built by MFMA (pr 4): 2.3-5.8% faster than the vector-ALU build at
+    // m = 2..32 on 12288 x 12288, with 26% fewer VALU instructions at m = 32.
     struct Cand { int w, rpw, mc; double eff, bar; int pr; int min_m; };
     const Cand cands[] = {
         {16, 2, 1, 1.0, 0.0, false, 1},    {16, 1, 1, 1.0, 0.0, false, 1},
-        {16, 1, 2, 0.5, 0.28, true, 2},   {8, 2, 4, 0.5, 0.425, true, 8},
+        {16, 1, 2, 0.5, 0.28, 4, 2},      {8, 2, 4, 0.5, 0.425, true, 8},
         {8, 1, 4, 0.5, 0.425, true, 8},    {8, 2, 2, 0.5, 0.425, true, 8},
         {8, 1, 2, 0.5, 0.425, true, 8},    {8, 2, 4, 0.71, 0.31, false, 4},
         {8, 1, 4, 0.71, 0.31, false, 4},   {8, 2, 2, 0.71, 0.31, false, 2},
@@ -277,7 +279,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
   } else if (have_o) {
     const int w = o.w ? o.w : c.W;
     const int mc = o.mc ? o.mc : c.MC;
-    const int pr = o.pr >= 1 && o.pr <= 3 ? o.pr : 0;
+    const int pr = o.pr >= 1 && o.pr <= 4 ? o.pr : 0;
     const bool xl = pr ? false
                     : o.xl < 0 ? xl_ok && pick_kernel(q, o.rpw, mc, c.gq, off, w, o.ring, true)
                                : (o.xl > 0 && xl_ok);
@@ -578,6 +580,7 @@ int lutgemm_query_plan(const lutgemm_shape* s, int32_t m, int32_t cus, size_t wo
     if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
     out->tables = c.us ? LUTGEMM_TABLES_NIBBLE
                   : c.pr == 3 ? LUTGEMM_TABLES_SPLIT
+                  : c.pr == 4 ? LUTGEMM_TABLES_PAIRED_MFMA
                   : c.pr == 2 ? LUTGEMM_TABLES_HALF
                   : c.pr == 1 ? LUTGEMM_TABLES_PAIRED
                               : LUTGEMM_TABLES_SINGLE;

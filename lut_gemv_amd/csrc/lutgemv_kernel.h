@@ -312,7 +312,10 @@ __device__ __forceinline__ void tile_group_offsets(const Params& p, LaneCtx& l) 
 // the loads of the planes share their lines, and a non-temporal line can be
 // gone before the next plane's load. With several batch groups the groups
 // re-read the same weights, which the caches then serve.
-template <int Q, int RPW, int MC, bool GQ, bool OFF, bool XL, bool NT>
+// MB: the tables are built by MFMA (build_pair_mfma); xv[h] then holds the B
+// operands of batch rows (2h, 2h+1) for this wave's two n-blocks instead of
+// chunk `lane` of each row.
+template <int Q, int RPW, int MC, bool GQ, bool OFF, bool XL, bool NT, bool MB = false>
 __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
                                           TileRegs<Q, RPW, MC, GQ, OFF>& T) {
   constexpr uint32_t kTileBytes = Q * kChunkTile * kRowTile;
@@ -323,7 +326,31 @@ __device__ __forceinline__ void load_tile(const Params& p, const LaneCtx& l,
   // bytes for this wave; the tile's position goes in the scalar offset (each
   // buffer is under 4 GiB). A dead position is an empty range.
   const uint32_t kin = t.live ? (uint32_t)min(kChunkTile * 8, p.K - k0) : 0u;
-  if constexpr (!XL) {   // (with XL the activations are in LDS)
+  if constexpr (MB) {
+    // lane l: column l % 32 of n-blocks nb0 and nb0 + 1, i.e. chunk
+    // 16 * nb + (l % 32) / 2 of row 2h + (l & 1), inputs 4 * (l / 32) .. + 3 of
+    // that chunk (8 bytes). One descriptor spans the pair's rows that exist;
+    // lanes past the input dimension or the batch read at its end (zero).
+    const uint32_t col = (uint32_t)(l.lane & 31), kh = (uint32_t)(l.lane >> 5);
+    const uint32_t rl = (uint32_t)(l.lane & 1);
+    const uint32_t nb0 = 2u * (uint32_t)(l.wave >> 3);
+    const uint32_t rowb = (uint32_t)p.K * 2u;
+#pragma unroll
+    for (int h = 0; h < MC / 2; ++h) {
+      const int rows = t.live ? min(2, t.c.rows_here - 2 * h) : 0;
+      const uint32_t span = rows > 0 ? (uint32_t)rows * rowb : 0u;
+      const uint32_t xs = ((uint32_t)(t.c.r0 + 2 * h) * (uint32_t)p.K + (uint32_t)k0) * 2u;
+      const auto rs = make_rsrc(p.x, span ? xs + span : 0u);
+      uint2 v[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t kk = 8u * (16u * (nb0 + (uint32_t)j) + col / 2u) + 4u * kh;
+        const bool ok = kk < kin && (int)rl < rows;
+        v[j] = load8(rs, ok ? rl * rowb + kk * 2u : span, xs);
+      }
+      T.xv[h] = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
+    }
+  } else if constexpr (!XL) {   // (with XL the activations are in LDS)
 #pragma unroll
     for (int r = 0; r < MC; ++r) {
       const uint32_t nb = (r < t.c.rows_here) ? kin * 2u : 0u;
@@ -474,6 +501,51 @@ __device__ __forceinline__ void build_table_pair(float* lut, const LaneCtx& l, c
     T += ((pat >> t) & 1) ? twx[t] : -twx[t];
     U += ((pat >> t) & 1) ? twy[t] : -twy[t];
     *reinterpret_cast<float2*>(base + pat * 256) = make_float2(T, U);
+  }
+}
+
+// ------------------------------------------------------------------ MFMA-built paired tables
+// The paired table of two batch rows is a dense product: entry p of column
+// (chunk t, row r) is sum_k S[p][k] x_r[8t + k] with S[p][k] = +1 if bit k of p
+// is set, else -1, a 256 x 8 sign matrix times the 8 x 128 matrix of the tile's
+// activations. v_mfma_f32_32x32x8f16 computes one 32 x 32 block of it from fp16
+// x (exact products, fp32 sums): wave w takes patterns 32 * (w % 8) .. + 31 and
+// n-blocks 2 * (w / 8) and + 1 (column n = 2 * (chunk % 16) + row, chunk
+// = 16 * nb + n / 2), two MFMAs per table and no vector-ALU arithmetic.
+// Operand layouts (32x32x8): A[i][k] in lane i + 32 * (k / 4), element k % 4;
+// B[k][j] in lane j + 32 * (k / 4), element k % 4; D[i][j] in lane
+// j + 32 * ((i / 4) % 2), register (i % 4) + 4 * (i / 8).
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+// The A operand of this wave: signs of pattern 32 * (w % 8) + l % 32, inputs
+// 4 * (l / 32) .. + 3.
+__device__ __forceinline__ half4v mfma_signs(const LaneCtx& l) {
+  const int pt = 32 * (l.wave & 7) + (l.lane & 31);
+  const int k0 = 4 * (l.lane >> 5);
+  half4v a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] = ((pt >> (k0 + e)) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
+  return a;
+}
+
+// This wave's part of the paired table of one pair of batch rows (xb: its B
+// operands, from load_tile with MB), written in the paired layout.
+__device__ __forceinline__ void build_pair_mfma(float* lut, const LaneCtx& l, const half4v a,
+                                                const uint4 xb) {
+  const int nb0 = 2 * (l.wave >> 3);
+  const int col = l.lane & 31;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const half4v b = __builtin_bit_cast(half4v, j ? make_uint2(xb.z, xb.w) : make_uint2(xb.x, xb.y));
+    float16v c = {};
+    c = __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, c, 0, 0, 0);
+    const int t = 16 * (nb0 + j) + col / 2;
+    char* base = reinterpret_cast<char*>(lut) + (32 * (l.wave & 7) + 4 * (l.lane >> 5)) * 256 +
+                 (t & 31) * 8 + (t >> 5) * (kLutWords * 4) + (col & 1) * 4;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      *reinterpret_cast<float*>(base + (8 * (v / 4) + (v % 4)) * 256) = c[v];
   }
 }
 
@@ -1057,8 +1129,9 @@ __device__ __forceinline__ void split_epilogue(const Params& p, int* s_last) {
 // tile takes two steps per pair of batch rows, one per half of its chunks,
 // each looking up one buffer, building the next step's table in the other and
 // ending at its one barrier.
+// MB (with PR, 16 waves): the paired tables are built by MFMA (build_pair_mfma).
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W, int NR, bool XL, bool PR = false,
-          bool EI = false, bool ONCE = false, bool HT = false, bool SP = false>
+          bool EI = false, bool ONCE = false, bool HT = false, bool SP = false, bool MB = false>
 // The 128 KiB of LDS allows one workgroup per CU, so W/4 waves per SIMD is
 // also the most that can ever run; saying so lets the scheduler use the
 // whole register budget to keep table lookups in flight.
@@ -1070,6 +1143,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   static_assert(!ONCE || (!XL && !PR && MC == 1), "read-once loads: batch 1 without x in LDS");
   static_assert(!HT || PR, "half tables are paired");
   static_assert(!SP || (PR && !HT && RPW == 1 && W == 16), "split paired tables: 16 waves x 1 row tile");
+  static_assert(!MB || (PR && !HT && !SP && W == 16), "MFMA-built tables: paired, 16 waves");
   LUTGEMM_PHASE(0);
   LUTGEMM_PHASE_FLAG(traced_table);
   LUTGEMM_PHASE_FLAG(traced_step);
@@ -1108,20 +1182,20 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   R[0].pos = first_tile<RPW, MC, W>(p, l.wave, blockIdx.x);
   if constexpr (XL) {
     if (!R[0].pos.live) return;
-    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[0]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, R[0]);
   } else {
     // The first tile's loads go ahead of the exit (a dead position touches no
     // memory), and the barrier keeps them there, so the buffer addresses they
     // need are fetched with the other kernel arguments in one round instead of
     // a third round after the exit.
-    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[0]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, R[0]);
     asm volatile("" ::: "memory");
     if (!R[0].pos.live) return;
   }
 #pragma unroll
   for (int s = 1; s + 1 < NR; ++s) {
     R[s].pos = next_tile<RPW, MC, W>(p, l.wave, R[s - 1].pos);
-    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[s]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, R[s]);
   }
   if constexpr (XL) {   // chunk c of x at xs[c], for the KT input tiles (zero past K)
     const int nchunks = p.KT * kChunkTile;
@@ -1139,7 +1213,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   // 3.6 us on 49152 x 12288; 0.3-1% faster on 32768-65536 rows).
   if constexpr (EI) {
     R[1].pos = next_tile<RPW, MC, W>(p, l.wave, R[0].pos);
-    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, R[1]);
+    load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, R[1]);
   }
   // activations of chunk `lane` of a tile, for the table build
   auto xtile = [&](const TR& T, int r) -> uint4 {
@@ -1165,7 +1239,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
           TR& nxt = R[(s + 1) % NR];
           TR& pre = R[(s + NR - 1) % NR];
           pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
-          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
+          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, pre);
           split_arrange<Q, MC, OFF>(cur);
 #pragma unroll
           for (int h = 0; h < MC / 2; ++h) {
@@ -1207,7 +1281,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
           TR& nxt = R[(s + 1) % NR];
           TR& pre = R[(s + NR - 1) % NR];
           pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
-          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
+          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, pre);
 #pragma unroll
           for (int h = 0; h < MC / 2; ++h) {
             if (2 * h < cur.pos.c.rows_here) {  // uniform over the workgroup
@@ -1233,6 +1307,8 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     LUTGEMM_PHASE(5);
     return;
   } else if constexpr (PR) {
+    half4v sgn = {};
+    if constexpr (MB) sgn = mfma_signs(l);
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -1242,12 +1318,16 @@ __global__ void __launch_bounds__(W * 64, W / 4)
           TR& nxt = R[(s + 1) % NR];
           TR& pre = R[(s + NR - 1) % NR];
           pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
-          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
+          load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, pre);
 #pragma unroll
           for (int h = 0; h < MC / 2; ++h) {
             if (2 * h < cur.pos.c.rows_here) {  // uniform over the workgroup
               __syncthreads();                  // the previous lookups are done
-              build_table_pair<W>(lut, l, cur.xv[2 * h], cur.xv[2 * h + 1]);
+              if constexpr (MB) {
+                build_pair_mfma(lut, l, sgn, cur.xv[h]);
+              } else {
+                build_table_pair<W>(lut, l, cur.xv[2 * h], cur.xv[2 * h + 1]);
+              }
               __syncthreads();
               LUTGEMM_PHASE_ONCE(2, traced_table);
               lookups_pair<Q, RPW, MC, OFF>(l, h, lut, cur, acc);
@@ -1277,7 +1357,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         const TilePos was = cur.pos;
         if (was.live) lookups(l, 0, buf, lut, cur, acc);   // uniform over the workgroup
         cur.pos = next_tile<RPW, MC, W>(p, l.wave, nxt.pos);
-        load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, cur);
+        load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, cur);
         if (was.live) {
           if (nxt.pos.live) build_table<W>(lut, buf ^ 1, l, xtile(nxt, 0));
           __syncthreads();
@@ -1302,7 +1382,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
         TR& nxt = R[(s + 1) % NR];
         TR& pre = R[(s + NR - 1) % NR];
         pre.pos = next_tile<RPW, MC, W>(p, l.wave, R[(s + NR - 2) % NR].pos);
-        load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE>(p, l, pre);
+        load_tile<Q, RPW, MC, GQ, OFF, XL, XL || ONCE, MB>(p, l, pre);
 #pragma unroll
         for (int r = 0; r < MC; ++r) {
           if (r < cur.pos.c.rows_here) {  // uniform over the workgroup
@@ -1681,12 +1761,21 @@ constexpr int kRingPair =
 // variant (default ring only); once the read-once (non-temporal) sign-plane
 // loads of the 16-wave batch-1 instances without x in LDS.
 // pr: 1 paired tables, 2 half paired tables (one row tile per wave only), 3
-// split paired tables (16 waves, one row tile per wave, two batch rows).
+// split paired tables (16 waves, one row tile per wave, two batch rows), 4
+// paired tables built by MFMA (16 waves).
 template <int Q, int RPW, int MC, bool GQ, bool OFF, int W>
 KernelFn kernel_or_null(int ring, bool xl, int pr, bool ei, bool once) {
   if (pr) {
     if constexpr (GQ && kRingPair<Q, RPW, MC, OFF, W> > 0) {
       if (xl) return nullptr;
+      if (pr == 4) {
+        if constexpr (W == 16) {
+          return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true,
+                                false, false, false, false, true>;
+        } else {
+          return nullptr;
+        }
+      }
       if (pr == 3) {
         if constexpr (RPW == 1 && W == 16 && MC == 2) {
           return lutgemv_kernel<Q, RPW, MC, GQ, OFF, W, kRingPair<Q, RPW, MC, OFF, W>, false, true,
@@ -1769,7 +1858,8 @@ KernelFn pick_rpw_mc(int rpw, int mc, bool gq, bool off, int ring, bool xl, int 
 // The instance for q = Q planes, rpw row tiles per wave, mc batch rows per
 // item, scale groups aligned to 32 inputs (gq), an offset term (off), w waves
 // per workgroup, ring depth (0 default, >= 3 deeper), x in LDS (xl), paired
-// tables (pr: 1 paired, 2 half paired, 3 split paired), the early-issue ring (ei) and read-once
+// tables (pr: 1 paired, 2 half paired, 3 split paired, 4 MFMA-built paired), the
+// early-issue ring (ei) and read-once
 // sign-plane loads (once), or nullptr if none is built.
 template <int Q>
 KernelFn kernels_of_q(int rpw, int mc, bool gq, bool off, int w, int ring, bool xl, int pr,

@@ -307,6 +307,30 @@ def test_split_paired_tables_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# PR = 4: paired tables built by MFMA (the sign matrix times the activations;
+# 16 waves, one row tile per wave, two batch rows: built for q <= 3)
+@pytest.mark.parametrize("tile", ["1,1,16,2,0,16,0,4", "1,3,16,2,0,11,0,4", "1,2,16,2,0,5,0,4"])
+@pytest.mark.parametrize("N,K,q,g,m,off", [
+    (1000, 4128, 3, 32, 3, True),      # ragged rows and input tiles, odd batch
+    (300, 1536, 2, 64, 5, False),
+    (1024, 12288, 3, 128, 4, False),
+    (129, 2048, 1, 256, 7, True),
+    (700, 1056, 2, 32, 1, True),       # one batch row; the last input tile holds 4 chunks
+    (513, 3072, 1, 512, 10, False),
+    (2000, 1536, 3, 1536, 2, True),    # one scale group per row
+])
+def test_mfma_built_tables_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + q + m + 13, with_offset=off,
+                             name=f"mfma_{N}x{K}q{q}g{g}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", tile)
+    if g % 32 == 0:
+        assert lg.query_plan(N, K, q, g, off, m)["tables"] == "paired_mfma"
+    _say(f"MFMA-built tables {tile}: N={N} K={K} q={q} g={g} m={m} offset={off}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
 # "RPW,S,W,MC,ring,RI,XL,PR,EI": x in LDS with the early-issue ring (EI = 1), forced
 # onto single-item, split and many-item launches, and the plain ring beside it (EI = 0)
 @pytest.mark.parametrize("tile", ["1,1,16,1,0,12,1,0,1", "1,1,16,1,0,12,1,0,0", "1,3,16,1,0,5,1,0,1",

@@ -119,7 +119,7 @@ def test_query_plan_batch_one_and_batched():
     assert c2["row_tiles"] * 256 >= 49152 // 16 and c2["workspace_bytes"] == 0
     for m in (2, 4, 16, 32):
         p = lg.query_plan(12288, 12288, 3, 128, False, m)
-        assert p["tables"] == "paired" and p["batch_rows"] == 2 and p["x_in_lds"] == 0, (m, p)
+        assert p["tables"] == "paired_mfma" and p["batch_rows"] == 2 and p["x_in_lds"] == 0, (m, p)
         assert p["workspace_bytes"] == lg.workspace_size(12288, 12288, 3, 128, False, m)
         assert p["workgroups"] == min(p["items"], 256)
     nib = lg.query_plan(4096, 4096, 3, 128, False, 1)
