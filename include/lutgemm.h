@@ -222,7 +222,10 @@ size_t lutgemm_noalloc_scratch_bytes(void);
  *                          time (32 chunks), two buffers;
  *   LUTGEMM_TABLES_PAIRED_MFMA  paired tables whose entries are computed by
  *                          matrix-core instructions (the 256 x 8 sign matrix
- *                          times the tile's activations).
+ *                          times the tile's activations);
+ *   LUTGEMM_TABLES_SIGN_MFMA  no tables: each sign plane times up to 32 batch
+ *                          rows of x on the matrix cores, the same signed sums
+ *                          per scale group (batches of several rows).
  * Fields of a plan with no launch (m == 0, N == 0 or K == 0) are zero.
  * Errors: NULL when s or out is NULL, SHAPE as for lutgemm_run or when
  * cus < 1, INTERNAL when no kernel instance fits. */
@@ -232,7 +235,8 @@ enum {
   LUTGEMM_TABLES_HALF = 2,
   LUTGEMM_TABLES_NIBBLE = 3,
   LUTGEMM_TABLES_SPLIT = 4,
-  LUTGEMM_TABLES_PAIRED_MFMA = 5
+  LUTGEMM_TABLES_PAIRED_MFMA = 5,
+  LUTGEMM_TABLES_SIGN_MFMA = 6
 };
 typedef struct lutgemm_plan {
   int32_t tables;         /* LUTGEMM_TABLES_*                                   */

@@ -44,7 +44,8 @@ class LutGemmError(RuntimeError):
         super().__init__(f"{where}: {self.name} ({status_string(status)})")
 
 
-TABLES = {0: "single", 1: "paired", 2: "half", 3: "nibble", 4: "split", 5: "paired_mfma"}
+TABLES = {0: "single", 1: "paired", 2: "half", 3: "nibble", 4: "split", 5: "paired_mfma",
+          6: "sign_mfma"}
 
 
 class _Plan(ctypes.Structure):

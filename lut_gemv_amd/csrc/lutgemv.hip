@@ -1,6 +1,7 @@
 // lutgemv.hip -- host side of the BCQ LUT-GEMV library: argument checks,
 // choice of kernel instance and work split, launch, and the C entry points
-// declared in lutgemm.h. The kernel itself is in lutgemv_kernel.h.
+// declared in lutgemm.h. The kernels are in lutgemv_kernel.h (tables) and
+// sign_mfma_kernel.h (the sign planes on the matrix cores).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -13,6 +14,7 @@
 #include "layout.h"
 #include "lutgemm.h"
 #include "lutgemv_kernel.h"
+#include "sign_mfma_kernel.h"
 
 namespace lutgemm {
 
@@ -77,6 +79,22 @@ KernelFn pick_nibble(int q, bool off, int upw, int nr) {
 }
 
 
+// The sign-plane MFMA kernel for q planes, cg groups of 16 batch rows, an
+// offset term, w waves and non-temporal sign loads, or nullptr.
+KernelFn pick_sign_mfma(int q, int cg, bool off, int w, bool nt) {
+  switch (q) {
+    case 1: return sign_mfma_kernel_of_q<1>(cg, off, w, nt);
+    case 2: return sign_mfma_kernel_of_q<2>(cg, off, w, nt);
+    case 3: return sign_mfma_kernel_of_q<3>(cg, off, w, nt);
+    case 4: return sign_mfma_kernel_of_q<4>(cg, off, w, nt);
+    case 5: return sign_mfma_kernel_of_q<5>(cg, off, w, nt);
+    case 6: return sign_mfma_kernel_of_q<6>(cg, off, w, nt);
+    case 7: return sign_mfma_kernel_of_q<7>(cg, off, w, nt);
+    case 8: return sign_mfma_kernel_of_q<8>(cg, off, w, nt);
+    default: return nullptr;
+  }
+}
+
 struct Config {
   int RPW, MC, S, W;
   int RI;                // row tiles per row block (<= W * RPW)
@@ -89,6 +107,7 @@ struct Config {
   bool once;             // batch 1 without x in LDS: non-temporal sign-plane loads
   bool us;               // the nibble-table unit kernel (batch 1, few row tiles per CU)
   int upw, nr;           // its units per wave and ring depth
+  bool mf;               // the sign-plane MFMA kernel (MC = 16 or 32 batch rows per item)
   int64_t n_rb, n_bg;
   bool gq;
   size_t ws_bytes;
@@ -108,7 +127,9 @@ struct TileOverride {
 // never needed for correctness. XL: 1 stages x in LDS where possible, 0 never
 // (default: where possible). PR: 1 paired tables, 2 half paired tables, 3
 // split paired tables, 4 paired tables built by MFMA, each where an instance
-// has them, 0 never (default: the dispatcher's choice). EI: 1 the early-issue ring where
+// has them, 5 the sign-plane MFMA kernel (with W waves, MC = 16 or 32 batch rows
+// per item and split S, 0 for its own choice; scale groups of whole 128-input
+// step groups), 0 never (default: the dispatcher's choice). EI: 1 the early-issue ring where
 // x is staged in LDS with the default ring, 0 never (the default). US: 1 the
 // nibble-table unit kernel where it applies (batch 1, scale groups dividing or
 // multiples of 512 inputs, x in LDS) with RI row tiles per workgroup (default:
@@ -120,6 +141,53 @@ bool tile_override(TileOverride* o) {
   const int n = sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &o->rpw, &o->s, &o->w, &o->mc,
                        &o->ring, &o->ri, &o->xl, &o->pr, &o->ei, &o->us);
   return n >= 2;
+}
+
+// The sign-plane MFMA launch (scale groups of whole 128-input step groups):
+// w waves of one row tile each per row block, cg groups of 16 batch rows per
+// item, and the split of the input tiles s_force, or (s_force < 1) the split
+// that gives the busiest CU the fewest tile steps, each item also paying about
+// two tile steps for its pipeline fill and a split two more for its reduction
+// (measured on 12288 x 12288 at m = 4: 85.3 us unsplit on 48 CUs, splits 2, 3,
+// 4, 5, 8: 49.8, 37.1, 30.8, 28.7, 36.4 us).
+// Sign loads are non-temporal when one batch group reads the weights once.
+bool mfma_config(const Geometry& G, int64_t m, int cus, size_t max_ws, int w, int cg,
+                 int64_t s_force, Config* out) {
+  if (G.g % 128 != 0 || cg < 1 || cg > 2) return false;
+  const int mc = 16 * cg;
+  const int64_t n_bg = (m + mc - 1) / mc;
+  if (!pick_sign_mfma((int)G.q, cg, G.has_offset, w, n_bg == 1)) return false;
+  const int64_t n_rb = (G.RT + w - 1) / w;
+  int64_t best_s = 1;
+  if (s_force >= 1) {
+    best_s = s_force < G.KT ? s_force : G.KT;
+  } else {
+    double best = 1e300;
+    const int64_t smax = G.KT < 64 ? G.KT : 64;
+    for (int64_t s = 1; s <= smax; ++s) {
+      if (s > 1 && split_ws_bytes(G, m, s) > max_ws) break;
+      const int64_t items = n_rb * n_bg * s;
+      const int64_t per_cu = (items + cus - 1) / cus;
+      const int64_t tiles = (G.KT + s - 1) / s;
+      const double cost = (double)per_cu * ((double)tiles + 2.0) + (s > 1 ? 2.0 : 0.0);
+      if (cost < best - 1e-9) {
+        best = cost;
+        best_s = s;
+      }
+    }
+  }
+  Config c{};
+  c.mf = true;
+  c.gq = true;
+  c.W = w;
+  c.RPW = 1;
+  c.MC = mc;
+  c.RI = w;
+  c.n_rb = n_rb;
+  c.n_bg = n_bg;
+  c.S = (int)best_s;
+  *out = c;
+  return true;
 }
 
 // Pick waves, rows per wave, batch rows per item, row tiles per item, the
@@ -276,6 +344,20 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
       c.ws_bytes = 0;
       return c;
     }
+  } else if (have_o && o.pr == 5) {
+    // the sign-plane MFMA kernel: W waves (default 16), MC = 16 or 32 batch
+    // rows per item (default: 32 from m = 17 on), split S (0: its own choice)
+    // (fields left at 0 fall back, in this order, to 8 waves and then to one
+    // group of 16 batch rows where an instance with more is not built)
+    Config f{};
+    const int cg = o.mc ? (o.mc > 16 ? 2 : 1) : (m > 16 ? 2 : 1);
+    bool ok = false;
+    for (int k = 0; k < 4 && !ok; ++k) {
+      const int w = k % 2 ? 8 : 16, g2 = k < 2 ? cg : 1;
+      if ((o.w && w != o.w) || (o.mc && g2 != cg)) continue;
+      ok = mfma_config(G, m, cus, max_ws, w, g2, o.s, &f);
+    }
+    if (ok) c = f;
   } else if (have_o) {
     const int w = o.w ? o.w : c.W;
     const int mc = o.mc ? o.mc : c.MC;
@@ -300,13 +382,23 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
     }
     if (o.s >= 1) c.S = (int)(o.s < G.KT ? o.s : (G.KT > 0 ? G.KT : 1));
   }
+  // From 4 batch rows on, with scale groups of whole 128-input step groups,
+  // the sign-plane MFMA kernel (16 waves, 16 batch rows per item where built):
+  // on 12288 x 12288 it measured 28.7 / 29.6 / 32.2 / 53.4 us at m = 4 / 8 /
+  // 16 / 32 against 33.2 / 51.9 / 93.0 / 170.4 us for the best table launch;
+  // at m = 2 the paired tables stay faster (21.2 against 28.1 us).
+  if (!have_o && m >= 4) {
+    Config f{};
+    if (mfma_config(G, m, cus, max_ws, 16, 1, 0, &f) || mfma_config(G, m, cus, max_ws, 8, 1, 0, &f))
+      c = f;
+  }
   if (c.S < 1) c.S = 1;
   if (c.S > 1 && split_ws_bytes(G, m, c.S) > max_ws) c.S = 1;
   if (c.n_rb * c.n_bg > kMaxCounters) c.S = 1;   // counters live in a fixed region
   // batch 1 without x in LDS: each sign byte is still read once per product
   // (where a read-once instance exists for the choice, it differs from the
   // ordinary one)
-  c.once = m == 1 && !c.xl && !c.pr && c.MC == 1 &&
+  c.once = m == 1 && !c.xl && !c.pr && !c.mf && c.MC == 1 &&
            pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, c.ring, false, false, false, true) !=
                pick_kernel(q, c.RPW, c.MC, c.gq, off, c.W, c.ring, false, false, false, false);
   c.ws_bytes = c.S > 1 ? split_ws_bytes(G, m, c.S) : 0;
@@ -400,8 +492,9 @@ int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d
            const void* d_alpha, const void* d_offset, const void* d_x, void* d_y, void* ws,
            hipStream_t strm) {
   KernelFn fn = c.us ? pick_nibble((int)G.q, G.has_offset, c.upw, c.nr)
-                     : pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl,
-                                   c.pr, c.ei, c.once);
+                : c.mf ? pick_sign_mfma((int)G.q, c.MC / 16, G.has_offset, c.W, c.n_bg == 1)
+                       : pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl,
+                                     c.pr, c.ei, c.once);
   if (!fn) return LUTGEMM_ERR_INTERNAL;
   Params p{};
   p.trace = g_trace.load(std::memory_order_relaxed);
@@ -435,7 +528,7 @@ int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d
   // measured 0.7-1.8 us faster at 2 and 3 batch groups of one-row items; at 4
   // it moved by -0.8..+0.3 us from one machine to another, and with paired tables at 4..16
   // groups it was slower (each round then streams few distinct blocks).
-  p.xcd_bg = (!c.pr && c.n_bg > 1 && c.n_bg <= 3 && (c.n_rb * c.S) % 8 == 0) ? 1 : 0;
+  p.xcd_bg = (!c.pr && !c.mf && c.n_bg > 1 && c.n_bg <= 3 && (c.n_rb * c.S) % 8 == 0) ? 1 : 0;
   const int64_t items = c.n_rb * c.n_bg * c.S;
   if (items > 0x7FFFFFFF - (int64_t)cus) return LUTGEMM_ERR_SHAPE;
   p.n_items = (int)items;
@@ -579,6 +672,7 @@ int lutgemm_query_plan(const lutgemm_shape* s, int32_t m, int32_t cus, size_t wo
     const Config c = choose_config(G, m, cus, workspace_bytes);
     if (c.W == 0) return LUTGEMM_ERR_INTERNAL;
     out->tables = c.us ? LUTGEMM_TABLES_NIBBLE
+                  : c.mf ? LUTGEMM_TABLES_SIGN_MFMA
                   : c.pr == 3 ? LUTGEMM_TABLES_SPLIT
                   : c.pr == 4 ? LUTGEMM_TABLES_PAIRED_MFMA
                   : c.pr == 2 ? LUTGEMM_TABLES_HALF

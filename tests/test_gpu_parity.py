@@ -331,6 +331,35 @@ def test_mfma_built_tables_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# PR = 5: the sign-plane MFMA kernel ("RPW,S,W,MC,...,PR": split S, W waves and
+# MC = 16 or 32 batch rows per item, 0 for the kernel's own choice): ragged
+# rows, input tiles with fewer than four step groups, several batch groups,
+# offsets, scale groups of 128..512 inputs, every plane count
+@pytest.mark.parametrize("tile", ["1,0,0,0,0,0,0,5", "1,1,0,16,0,0,0,5", "1,3,8,0,0,0,0,5",
+                                  "1,7,0,16,0,0,0,5"])
+@pytest.mark.parametrize("N,K,q,g,m,off", [
+    (1000, 4224, 3, 128, 4, False),    # the last input tile holds one step group
+    (300, 1536, 2, 256, 17, True),     # two groups of 16 batch rows
+    (1024, 12288, 3, 128, 32, False),
+    (129, 3072, 1, 384, 7, True),      # groups straddle input tiles
+    (700, 1536, 4, 512, 2, True),
+    (513, 4096, 8, 128, 40, False),    # three batch groups of 16
+    (250, 2560, 6, 128, 33, True),
+    (64, 512, 3, 128, 3, False),
+    (700, 1024, 5, 128, 1, False),     # one batch row
+])
+def test_sign_mfma_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + 7 * q + m, with_offset=off,
+                             name=f"signmfma_{N}x{K}q{q}g{g}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", tile)
+    plan = lg.query_plan(N, K, q, g, off, m)
+    assert plan["tables"] == "sign_mfma", plan
+    _say(f"sign MFMA {tile}: N={N} K={K} q={q} g={g} m={m} offset={off} plan={plan}")
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
 # "RPW,S,W,MC,ring,RI,XL,PR,EI": x in LDS with the early-issue ring (EI = 1), forced
 # onto single-item, split and many-item launches, and the plain ring beside it (EI = 0)
 @pytest.mark.parametrize("tile", ["1,1,16,1,0,12,1,0,1", "1,1,16,1,0,12,1,0,0", "1,3,16,1,0,5,1,0,1",

@@ -119,9 +119,16 @@ def test_query_plan_batch_one_and_batched():
     assert c2["row_tiles"] * 256 >= 49152 // 16 and c2["workspace_bytes"] == 0
     for m in (2, 4, 16, 32):
         p = lg.query_plan(12288, 12288, 3, 128, False, m)
-        assert p["tables"] == "paired_mfma" and p["batch_rows"] == 2 and p["x_in_lds"] == 0, (m, p)
+        if m == 2:
+            assert p["tables"] == "paired_mfma" and p["batch_rows"] == 2 and p["x_in_lds"] == 0, p
+        else:   # the sign-plane MFMA kernel from 4 batch rows on
+            assert p["tables"] == "sign_mfma" and p["batch_rows"] == 16 and p["waves"] == 16, p
+            S = 5 if m <= 16 else 2   # measured best: 28.7 us at m = 4, 53.4 at m = 32
+            assert p["split"] == S and p["items"] == 48 * S * -(-m // 16), p
         assert p["workspace_bytes"] == lg.workspace_size(12288, 12288, 3, 128, False, m)
         assert p["workgroups"] == min(p["items"], 256)
+    # scale groups that are not whole 128-input step groups keep the tables
+    assert lg.query_plan(12288, 12288, 3, 64, False, 8)["tables"] != "sign_mfma"
     nib = lg.query_plan(4096, 4096, 3, 128, False, 1)
     assert nib["tables"] == "nibble" and nib["split"] == 1 and nib["workgroups"] == nib["items"]
     # scale groups not aligned to 32 inputs: single-row tables
@@ -144,6 +151,24 @@ def test_query_plan_limits_and_override(monkeypatch):
     assert (half["tables"], half["split"], half["batch_rows"], half["waves"]) == ("half", 4, 2, 16)
     monkeypatch.setenv("LUTGEMM_TILE", "0,1,16,1,0,3,1,0,0,1")
     assert lg.query_plan(11008, 4096, 4, 128, True, 1)["tables"] == "nibble"
+    monkeypatch.delenv("LUTGEMM_TILE")
+    # the sign-plane MFMA kernel forced (PR = 5): an instance exists for every
+    # plane count, offset and batch (fewer waves or batch rows per item where
+    # the larger ones are not built); scale groups must be whole 128-input
+    # step groups, else the override is ignored
+    monkeypatch.setenv("LUTGEMM_TILE", "1,0,0,0,0,0,0,5")
+    for q in range(1, 9):
+        for off in (False, True):
+            for m in (1, 2, 16, 17, 40):
+                p = lg.query_plan(700, 2048, q, 128, off, m)
+                assert p["tables"] == "sign_mfma" and p["waves"] in (8, 16), (q, off, m, p)
+                assert p["batch_rows"] in (16, 32) and p["row_tiles"] == p["waves"], p
+                assert p["workspace_bytes"] == (0 if p["split"] == 1 else
+                                                65536 + 4 * p["split"] * m * 704)
+    assert lg.query_plan(700, 2048, 3, 64, False, 4)["tables"] != "sign_mfma"
+    monkeypatch.setenv("LUTGEMM_TILE", "1,3,8,32,0,0,0,5")
+    p = lg.query_plan(12288, 12288, 3, 128, False, 40)
+    assert (p["waves"], p["batch_rows"], p["split"], p["items"]) == (8, 32, 3, 1536 * 2 * 3 // 8 // 2)
     monkeypatch.delenv("LUTGEMM_TILE")
     L = lg.lib()
     pl = lg._Plan()

@@ -75,7 +75,7 @@ def test_noalloc_two_calls_second_smaller():
 def test_noalloc_split_limited_to_the_scratch():
     """A batch whose best split needs more than the scratch holds: the no-alloc
     call uses a split that fits (or none) and stays within tolerance."""
-    w = workloads.random_bcq(12288, 16384, 3, 128, m=24, seed=53, name="noalloc_m24")
+    w = workloads.random_bcq(12288, 16384, 3, 128, m=48, seed=53, name="noalloc_m48")
     need = lg.workspace_size(w.N, w.K, w.q, w.g, False, w.m)
     _say(f"{w.name}: lutgemm_run workspace {need} B, scratch {lg.noalloc_scratch_bytes()} B")
     assert need > lg.noalloc_scratch_bytes()
