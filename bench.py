@@ -11,9 +11,12 @@ Prints ONE JSON line on stdout. ``value`` is the achieved algorithmic HBM rate
 (GB/s) over the wall-clock timed region; ``roofline.achieved`` is the same work
 over the average launch duration, from a HIP event pair recorded on the launch
 stream around the same region. ``roofline.bound`` is the larger of the two
-algorithmic floors of the workload: HBM bytes at 8 TB/s, or fp32 arithmetic
-(two flops per lookup, the tables built once) at the non-packed fp32 vector
-rate of 78.6 TFLOP/s.
+algorithmic floors of the workload: HBM bytes at 8 TB/s, or the arithmetic of
+the kernel that runs: fp32 lookups (two flops per lookup, the tables built
+once) at the non-packed fp32 vector rate of 78.6 TFLOP/s for the table
+kernels, fp16 products of the sign planes with x at the dense 2.5 PFLOP/s
+matrix-core rate for the sign-plane MFMA kernel (batches of four rows and
+more).
 Before the ``--warmup`` launches, untimed launches run for at least
 ``--settle-s`` seconds and one full pass over the rotating weight copies, so
 that clocks and caches are in their steady state however short the warm-up is
@@ -38,8 +41,11 @@ HBM_PEAK_GBS = 8000.0
 # per compute unit, 256 CUs at 2.4 GHz, an FMA counting two flops (the 157.3
 # TFLOP/s figure counts packed FMAs, which this code does not use)
 ALU_PEAK_TFLOPS = 256 * 2.4e9 * 64 * 2 / 1e12
+# dense fp16 matrix-core peak of MI355X (no sparsity), for the sign-plane MFMA kernel
+MFMA_F16_PEAK_TFLOPS = 2500.0
 KERNEL_SRCS = [os.path.join(ROOT, "lut_gemv_amd", "csrc", f)
-               for f in ("lutgemv_kernel.h", "lutgemv_q.hip", "lutgemv.hip", "layout.h")]
+               for f in ("lutgemv_kernel.h", "sign_mfma_kernel.h", "lutgemv_q.hip", "lutgemv.hip",
+                         "layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lutgemv_traffic.json")
 
 
@@ -64,6 +70,13 @@ def algorithmic_flops(N, K, q, g, m, has_offset):
     if has_offset:
         f += 2 * m * N * (K // g)
     return f
+
+
+def mfma_flops(N, K, q, m, has_offset):
+    """Matrix-core work of the sign-plane MFMA kernel: each of the q sign planes
+    (and, with an offset, an all-ones plane) times the m batch rows of x, two
+    flops per product (the padding of the batch to 16 columns not counted)."""
+    return 2 * m * N * K * (q + (1 if has_offset else 0))
 
 
 def kernel_hash():
@@ -310,29 +323,54 @@ def main():
         f"launch on the GPU clock; single-launch events: p10 {p10:.2f} us, median {p50:.2f}, "
         f"p90 {p90:.2f}")
 
+    plan = None
+    if args.kernel == "lut":
+        # the launch lutgemm_run makes here (after LUTGEMM_TILE, if set)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        ws = None if cus == 256 else lg.workspace_size(w.N, w.K, w.q, w.g, bool(has_off), w.m)
+        plan = lg.query_plan(w.N, w.K, w.q, w.g, bool(has_off), w.m, cus=cus, workspace_bytes=ws)
+    on_mfma = plan is not None and plan["tables"] == "sign_mfma"
+
     ms_per_step = t_total * 1e3 / K_steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved_gbs = nbytes / avg_kernel_s / 1e9
     achieved_tflops = nflops / avg_kernel_s / 1e12
     hbm_frac = achieved_gbs / HBM_PEAK_GBS
     alu_frac = achieved_tflops / ALU_PEAK_TFLOPS
-    # the bound is the larger of the two algorithmic floors
+    # the bound is the larger of the two algorithmic floors: HBM bytes, and the
+    # arithmetic of the kernel that runs (fp32 lookups and table builds on the
+    # vector ALUs for the table kernels; fp16 products on the matrix cores for
+    # the sign-plane MFMA kernel)
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_alu = nflops / (ALU_PEAK_TFLOPS * 1e12)
-    if t_hbm >= t_alu or args.kernel == "stream":
+    mflops = mfma_flops(w.N, w.K, w.q, w.m, bool(has_off))
+    t_mfma = mflops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    mfma_frac = mflops / avg_kernel_s / 1e12 / MFMA_F16_PEAK_TFLOPS
+    t_comp = t_mfma if on_mfma else t_alu
+    if t_hbm >= t_comp or args.kernel == "stream":
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(hbm_frac, 4)}
+    elif on_mfma:
+        roof = {"bound": "mfma", "achieved": round(mflops / avg_kernel_s / 1e12, 3),
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
     else:
         roof = {"bound": "alu", "achieved": round(achieved_tflops, 3),
                 "peak": round(ALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s", "frac": round(alu_frac, 4)}
     # counters were taken with the default rotation (weights streamed from HBM)
     roof["traffic"] = (stored_traffic(w.name) if args.kernel == "lut" and args.rotate == 0
                        else None)
-    roof["floor_us"] = {"hbm": round(t_hbm * 1e6, 3), "alu": round(t_alu * 1e6, 3)}
-    roof["hbm_frac"] = round(hbm_frac, 4)
-    roof["alu_frac"] = round(alu_frac, 4)
-    roof["algorithmic_bytes"] = nbytes
-    roof["algorithmic_flops"] = nflops
+    if on_mfma:
+        roof["floor_us"] = {"hbm": round(t_hbm * 1e6, 3), "mfma": round(t_mfma * 1e6, 3)}
+        roof["hbm_frac"] = round(hbm_frac, 4)
+        roof["mfma_frac"] = round(mfma_frac, 4)
+        roof["algorithmic_bytes"] = nbytes
+        roof["algorithmic_flops"] = mflops
+    else:
+        roof["floor_us"] = {"hbm": round(t_hbm * 1e6, 3), "alu": round(t_alu * 1e6, 3)}
+        roof["hbm_frac"] = round(hbm_frac, 4)
+        roof["alu_frac"] = round(alu_frac, 4)
+        roof["algorithmic_bytes"] = nbytes
+        roof["algorithmic_flops"] = nflops
 
     if not args.no_stream_peak and args.kernel != "stream":
         peak_meas = stream_peak(lg, torch, dev)
@@ -356,12 +394,6 @@ def main():
                           f"{full1:.2f} s/GEMV ({nbytes / full1 / 1e9:.4f} GB/s)")}
         log(f"cpu baseline: {cpu['sample']}")
 
-    plan = None
-    if args.kernel == "lut":
-        # the launch lutgemm_run makes here (after LUTGEMM_TILE, if set)
-        cus = torch.cuda.get_device_properties(0).multi_processor_count
-        ws = None if cus == 256 else lg.workspace_size(w.N, w.K, w.q, w.g, bool(has_off), w.m)
-        plan = lg.query_plan(w.N, w.K, w.q, w.g, bool(has_off), w.m, cus=cus, workspace_bytes=ws)
     out = {
         "metric": (METRIC if w.name == "opt175b_ffn_up" and args.kernel == "lut"
                    else f"us/GEMV + achieved HBM GB/s, {w.name}, {args.kernel} kernel"),
@@ -380,7 +412,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16" if on_mfma else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "kernel": args.kernel,
                    "N": w.N, "K": w.K, "q": w.q, "g": w.g, "m": w.m,
