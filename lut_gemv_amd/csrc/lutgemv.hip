@@ -161,11 +161,15 @@ bool mfma_config(const Geometry& G, int64_t m, int cus, size_t max_ws, int w, in
   int64_t best_s = 1;
   if (s_force >= 1) {
     best_s = s_force < G.KT ? s_force : G.KT;
+    if ((uint64_t)best_s * (uint64_t)m * (uint64_t)G.Npad * 4u > 0xFFFFFFFFull) best_s = 1;
   } else {
     double best = 1e300;
     const int64_t smax = G.KT < 64 ? G.KT : 64;
     for (int64_t s = 1; s <= smax; ++s) {
-      if (s > 1 && split_ws_bytes(G, m, s) > max_ws) break;
+      // (the kernel addresses its partials with 32-bit offsets)
+      if (s > 1 && (split_ws_bytes(G, m, s) > max_ws ||
+                    (uint64_t)s * (uint64_t)m * (uint64_t)G.Npad * 4u > 0xFFFFFFFFull))
+        break;
       const int64_t items = n_rb * n_bg * s;
       const int64_t per_cu = (items + cus - 1) / cus;
       const int64_t tiles = (G.KT + s - 1) / s;

@@ -18,8 +18,9 @@
 // Mapping onto CDNA4 (our design):
 //  * a workgroup of W wave64s takes a row block of W row tiles (one per wave)
 //    over a range of input tiles (512 inputs) for up to 16 * CG batch rows;
-//    items (row block, input split, batch group) are walked persistently, and
-//    a split input dimension is reduced by the LUT kernels' fused epilogue;
+//    items (row block, input split, batch group) are walked persistently; a
+//    split input dimension is reduced by a fused epilogue like the table
+//    kernels', with 128-bit write-through partial stores and loads;
 //  * operand layout of the 16x16x32 f16 MFMA: lane l holds row l % 16 of A
 //    and column l % 16 of B, each with 8 consecutive k of k-group l / 16; the
 //    result D[i][j] is in lane j + 16 * (i / 4), register i % 4. Only the
@@ -70,6 +71,7 @@ constexpr int kSignMfmaLds = kSignTableBytes + 2 * kXBufBytes<CG> + 2 * W * kSBu
 
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 // Everything one wave needs from memory for one input tile.
 template <int Q, int CG, bool OFF, int W>
@@ -247,30 +249,105 @@ __device__ __forceinline__ void mfma_tile(const Params& p, const uint8_t* smem, 
   }
 }
 
+// Cache policy of the split partials' loads and stores: sc1, device scope (a
+// store is written through to the coherence point every XCD reads, a load
+// reads there rather than a possibly stale L2 line).
+constexpr int kDeviceScope = 16;
+
 // Store a finished item's accumulators (fp16 y, or this split's fp32
-// partials) and clear them.
+// partials, four rows of one batch row in one 128-bit write-through store)
+// and clear them. The partials [S][m][Npad] are under 4 GiB (the launcher
+// checks), so one descriptor covers them.
 template <int CG>
 __device__ __forceinline__ void mfma_finish(const Params& p, int lane, const ItemCtx& c,
                                             float (&acc)[CG][4]) {
   const int jg = lane >> 4;
+  const int row0 = c.rt_first * kRowTile + 4 * jg;
+  const auto pr = make_rsrc(p.partial, p.S > 1 ? (uint32_t)p.S * (uint32_t)p.m * (uint32_t)p.Npad * 4u : 0u);
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     const int col = (lane & 15) + 16 * cg;
     if (c.nrt > 0 && col < c.rows_here) {
+      if (p.S > 1) {
+        const uint32_t off =
+            (((uint32_t)c.split * (uint32_t)p.m + (uint32_t)(c.r0 + col)) * (uint32_t)p.Npad + (uint32_t)row0) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4v, float4v{acc[cg][0], acc[cg][1], acc[cg][2], acc[cg][3]}), pr, off, 0,
+            kDeviceScope);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = c.rt_first * kRowTile + 4 * jg + r;
-        if (p.S > 1) {
-          // device-scope store: written through to where every XCD reads it
-          __hip_atomic_store(&p.partial[((size_t)c.split * p.m + (c.r0 + col)) * p.Npad + row],
-                             acc[cg][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (row < p.N) {
-          p.y[(size_t)(c.r0 + col) * p.N + row] = __builtin_bit_cast(uint16_t, (_Float16)acc[cg][r]);
-        }
+        for (int r = 0; r < 4; ++r)
+          if (row0 + r < p.N)
+            p.y[(size_t)(c.r0 + col) * p.N + row0 + r] = __builtin_bit_cast(uint16_t, (_Float16)acc[cg][r]);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[cg][r] = 0.f;
+  }
+}
+
+// The split reduction of this kernel, run once after a workgroup's last item:
+// the arrival counting of split_epilogue (the same order argument: the
+// partial stores above are write-through, every wave waits for them before
+// the barrier and the counting), then the last arrival of an item's row block
+// adds its S partials in split order, four rows of one batch row per thread
+// with 128-bit loads (eight splits in flight), rounds to fp16 and stores y.
+template <int MC, int W>
+__device__ __forceinline__ void mfma_split_epilogue(const Params& p, int* s_last) {
+  constexpr int kThreads = W * 64;
+  const int kRows = p.ri * kRowTile;
+  const int kQuads = kRows / 4;
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt = expcnt = lgkmcnt = 0: own stores complete
+  __syncthreads();
+  const auto pr = make_rsrc(p.partial, (uint32_t)p.S * (uint32_t)p.m * (uint32_t)p.Npad * 4u);
+  const uint32_t sstride = (uint32_t)p.m * (uint32_t)p.Npad * 4u;
+  const int n_mine = (p.n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  for (int j0 = 0; j0 < n_mine; j0 += kThreads) {
+    const int nj = min(kThreads, n_mine - j0);
+    if ((int)threadIdx.x < nj) {
+      const int item = (int)blockIdx.x + (j0 + (int)threadIdx.x) * (int)gridDim.x;
+      int bg, split, rb;
+      decode_item(p, item, bg, split, rb);
+      uint32_t* ctr = p.counters + (size_t)bg * p.n_rb + rb;
+      const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (uint32_t)(p.S - 1);
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last[threadIdx.x] = last ? item : -1;
+    }
+    __syncthreads();
+    const int per_item = MC * kQuads;
+    for (int idx = threadIdx.x; idx < nj * per_item; idx += kThreads) {
+      const int j = idx / per_item;
+      const int item = s_last[j];
+      if (item < 0) continue;
+      const int rem = idx - j * per_item;
+      const int col = rem / kQuads;
+      int bg, split, rb;
+      decode_item(p, item, bg, split, rb);
+      const int row = rb * kRows + 4 * (rem - col * kQuads);
+      const int rr = bg * MC + col;
+      if (row >= p.N || rr >= p.m) continue;
+      const uint32_t off = ((uint32_t)rr * (uint32_t)p.Npad + (uint32_t)row) * 4u;
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < p.S; s0 += 8) {
+        float4v v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int sp = min(s0 + u, p.S - 1);   // past the last split: a valid slot, unused
+          v[u] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 pr, off + (uint32_t)sp * sstride, 0, kDeviceScope));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < p.S)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[e] += v[u][e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (row + e < p.N) p.y[(size_t)rr * p.N + row + e] = __builtin_bit_cast(uint16_t, (_Float16)sum[e]);
+    }
+    __syncthreads();
   }
 }
 
@@ -366,7 +443,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     trip(S[2], S[1], S[0].pos);
   }
   LUTGEMM_PHASE(4);
-  if (p.S > 1) split_epilogue<1, MC, W>(p, reinterpret_cast<int*>(smem));
+  if (p.S > 1) mfma_split_epilogue<MC, W>(p, reinterpret_cast<int*>(smem));
   LUTGEMM_PHASE(5);
 }
 
