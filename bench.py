@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -80,11 +81,17 @@ def mfma_flops(N, K, q, m, has_offset):
 
 
 def kernel_hash():
-    """Hash of the kernel and launcher sources (traffic counters go stale when they change)."""
+    """Hash of the kernel and launcher sources with their comments and blank
+    lines removed (traffic counters go stale when the code changes, not when a
+    comment does)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 

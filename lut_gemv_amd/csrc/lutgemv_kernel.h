@@ -40,7 +40,11 @@
 //    the last arrival of a row block adds its partials in split order (so
 //    results are bitwise reproducible). This avoids the L2-wide writeback and
 //    invalidate that release/acquire fences cost across the XCDs;
-//  * no MFMA: this is a lookup-accumulate, not a dense contraction.
+//  * the lookup is a gather, not a dense product, and stays on the vector
+//    ALUs and LDS; the paired tables of two batch rows can be built on the
+//    matrix cores (the 256 x 8 sign matrix times the tile's activations), and
+//    from 4 batch rows on the launcher uses the sign-plane MFMA kernel
+//    (sign_mfma_kernel.h) instead of the tables.
 //
 // Device code only. Each plane count q is instantiated in its own translation
 // unit (lutgemv_q.hip compiled with -DLUTGEMM_Q=q) so that the instances build
