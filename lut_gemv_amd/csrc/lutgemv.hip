@@ -290,6 +290,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
         {8, 1, 4, 0.71, 0.31, false, 4},   {8, 2, 2, 0.71, 0.31, false, 2},
         {8, 1, 2, 0.71, 0.31, false, 2},   {8, 2, 1, 1.3, 0.0, false, 1},
         {8, 1, 1, 1.3, 0.0, false, 1}};
+    double best_eff = 1.0;
     for (const Cand& v : cands) {
       if (m < v.min_m) continue;
       if (!pick_kernel(q, v.rpw, v.mc, c.gq, off, v.w, 0, false, v.pr)) continue;
@@ -310,6 +311,7 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
         const double cost = (double)per_cu * (tiles * step + fix) + (s > 1 ? 2.0 : 0.0);
         if (cost < best - 1e-9) {
           best = cost;
+          best_eff = v.eff;
           c.W = v.w;
           c.RPW = v.rpw;
           c.MC = v.mc;
@@ -317,6 +319,50 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
           c.RI = (int)rows;
           c.n_rb = n_rb;
           c.n_bg = n_bg;
+          c.S = (int)s;
+        }
+      }
+    }
+    // Batch 1: a row block of 8 to 16 row tiles on 16 waves, sized so that the
+    // items of a split just fill the compute units (waves past the block's row
+    // tiles only help build the tables). Compared with the choice above by the
+    // same cost with a fixed cost per tile step added (0.6 of a 16-row-tile
+    // step: the latency of a step that does not depend on its bytes), which
+    // the choice above leaves out. Measured: on 6144 x 12288 with the bytes
+    // per CU held fixed, 3 steps of 12 row tiles 11.4 us against 6 steps of 6
+    // 13.6 us; on 12288 x 12288, 5 steps of 16 row tiles (240 items) 15.9 us
+    // against 6 steps of 12 (256 items) 16.3 us. Chosen by it: 22016 x 4096
+    // (q = 3) 12.8 against 14.0 us, 28672 x 8192 (q = 4, g = 32) 32.6 against
+    // 36.1, 6144 x 12288 11.5 against 11.9, 12288 x 4096 9.7 against 9.9.
+    if (m == 1 && c.W > 0 && !c.pr && c.MC == 1 &&
+        pick_kernel(q, 1, 1, c.gq, off, 16, 0, false, 0) != nullptr) {
+      constexpr double kStepFix = 0.6;
+      auto cost_of = [&](int64_t rows, int64_t s, double eff) {
+        const int64_t items = ((G.RT + rows - 1) / rows) * s;
+        const int64_t per_cu = (items + cus - 1) / cus;
+        const int64_t tiles = (G.KT + s - 1) / s;
+        const double unit = eff * (double)rows / 16.0;
+        return (double)per_cu * (tiles * (unit + kStepFix) + 0.3 * unit) + (s > 1 ? 2.0 : 0.0);
+      };
+      double best2 = cost_of(c.RI, c.S, best_eff);
+      const int64_t smax = G.KT < 64 ? G.KT : 64;
+      for (int64_t s = 1; s <= smax && s <= cus; ++s) {
+        if (s > 1 && split_ws_bytes(G, m, s) > max_ws) break;
+        const int64_t per_s = cus / s;
+        int64_t ri = (G.RT + per_s - 1) / per_s;
+        ri = ri < 8 ? 8 : (ri > 16 ? 16 : ri);
+        const int64_t n_rb = (G.RT + ri - 1) / ri;
+        if (n_rb > kMaxCounters) continue;
+        const double cost = cost_of(ri, s, 1.0);
+        if (cost < best2 - 1e-9) {
+          best2 = cost;
+          c.W = 16;
+          c.RPW = 1;
+          c.MC = 1;
+          c.pr = 0;
+          c.RI = (int)ri;
+          c.n_rb = n_rb;
+          c.n_bg = 1;
           c.S = (int)s;
         }
       }
