@@ -131,6 +131,20 @@ def test_query_plan_batch_one_and_batched():
     assert lg.query_plan(12288, 12288, 3, 64, False, 8)["tables"] != "sign_mfma"
     nib = lg.query_plan(4096, 4096, 3, 128, False, 1)
     assert nib["tables"] == "nibble" and nib["split"] == 1 and nib["workgroups"] == nib["items"]
+    # batch 1 with a split: row blocks of 8-16 row tiles sized so that the
+    # split's items fill the 256 CUs (measured faster than 16-row blocks that
+    # leave CUs idle: the one-of-eight shard, the int4 MLP, 22016 x 4096)
+    for (N, K, q, g, off, ri, S) in ((6144, 12288, 3, 128, False, 12, 8),
+                                     (11008, 4096, 4, 128, True, 11, 4),
+                                     (22016, 4096, 3, 128, False, 11, 2)):
+        p = lg.query_plan(N, K, q, g, off, 1)
+        RT = N // 16
+        assert p["tables"] == "single" and p["waves"] == 16 and p["x_in_lds"] == 1, p
+        assert (p["row_tiles"], p["split"]) == (ri, S), p
+        assert 0.9 * 256 < p["items"] == -(-RT // ri) * S <= 256, p
+    # ... but not where fewer, longer steps measured faster (12288 x 12288)
+    p = lg.query_plan(12288, 12288, 3, 128, False, 1)
+    assert (p["row_tiles"], p["split"], p["items"]) == (16, 5, 240), p
     # scale groups not aligned to 32 inputs: single-row tables
     assert lg.query_plan(4096, 3072, 3, 24, False, 4)["tables"] == "single"
     for off in (False, True):
