@@ -207,38 +207,87 @@ __device__ __forceinline__ void mfma_tile(const Params& p, const uint8_t* smem, 
       const float4v zero = {0.f, 0.f, 0.f, 0.f};
       float4v D[Q][CG];
       float4v D1[CG];
+      uint2 a2[Q], o2;   // the group's scales (and offsets)
+      auto read_scales = [&]() {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        half8v B[CG];
-#pragma unroll
-        for (int c = 0; c < CG; ++c)
-          B[c] = *reinterpret_cast<const half8v*>(xb + c * 16 * kXRowBytes + 256 * u + 16 * b);
-        const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)b) << 8);
-#pragma unroll
-        for (int i = 0; i < Q; ++i) {
-          const uint32_t addr = __builtin_amdgcn_perm(T.sw[i][u], cb, sel);
-          const half8v A = *reinterpret_cast<const half8v*>(smem + addr);
+        for (int i = 0; i < Q; ++i) a2[i] = *reinterpret_cast<const uint2*>(sb + (gu * Q + i) * 32);
+        if constexpr (OFF) o2 = *reinterpret_cast<const uint2*>(sb + kStepGroups * Q * 32 + gu * 32);
+      };
+      // Where the registers allow a second operand set (at most 3 planes per
+      // group of 16 batch rows at 16 waves, 6 at 8 waves, the offset counted
+      // as a plane), the four steps are software-pipelined: the operand reads
+      // of step b + 1 (its B pieces of x, its A sign vectors; the scales in
+      // the last step's place) are issued before the MFMAs of step b, and
+      // scheduling barriers keep that order, so an MFMA waits only for reads
+      // issued a step earlier. Left to itself the compiler issues each read
+      // just before the MFMA that takes it, and every MFMA waits for a full
+      // LDS round trip; that is still the order where the set does not fit.
+      constexpr bool kPipe = (Q + (OFF ? 1 : 0)) * CG <= (W == 16 ? 3 : 6);
+      if constexpr (kPipe) {
+        half8v A[2][Q], B[2][CG];
+        auto read_step = [&](int b, int slot) {
 #pragma unroll
           for (int c = 0; c < CG; ++c)
-            D[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[c], b ? D[i][c] : zero, 0, 0, 0);
+            B[slot][c] = *reinterpret_cast<const half8v*>(xb + c * 16 * kXRowBytes + 256 * u + 16 * b);
+          const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)b) << 8);
+#pragma unroll
+          for (int i = 0; i < Q; ++i)
+            A[slot][i] = *reinterpret_cast<const half8v*>(smem + __builtin_amdgcn_perm(T.sw[i][u], cb, sel));
+        };
+        read_step(0, 0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b < 3) {
+            read_step(b + 1, (b + 1) & 1);
+          } else {
+            read_scales();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < Q; ++i)
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+              D[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[b & 1][i], B[b & 1][c], b ? D[i][c] : zero, 0, 0, 0);
+          if constexpr (OFF) {
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+              D1[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, B[b & 1][c], b ? D1[c] : zero, 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (OFF) {
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          half8v B[CG];
 #pragma unroll
           for (int c = 0; c < CG; ++c)
-            D1[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, B[c], b ? D1[c] : zero, 0, 0, 0);
+            B[c] = *reinterpret_cast<const half8v*>(xb + c * 16 * kXRowBytes + 256 * u + 16 * b);
+          const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)b) << 8);
+#pragma unroll
+          for (int i = 0; i < Q; ++i) {
+            const uint32_t addr = __builtin_amdgcn_perm(T.sw[i][u], cb, sel);
+            const half8v A = *reinterpret_cast<const half8v*>(smem + addr);
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+              D[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[c], b ? D[i][c] : zero, 0, 0, 0);
+          }
+          if constexpr (OFF) {
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+              D1[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, B[c], b ? D1[c] : zero, 0, 0, 0);
+          }
         }
+        read_scales();
       }
 #pragma unroll
       for (int i = 0; i < Q; ++i) {
-        const uint2 a2 = *reinterpret_cast<const uint2*>(sb + (gu * Q + i) * 32);
 #pragma unroll
         for (int c = 0; c < CG; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[c][r] = fmaf(h2f(r < 2 ? a2.x : a2.y, r & 1), D[i][c][r], acc[c][r]);
+            acc[c][r] = fmaf(h2f(r < 2 ? a2[i].x : a2[i].y, r & 1), D[i][c][r], acc[c][r]);
       }
       if constexpr (OFF) {
-        const uint2 o2 = *reinterpret_cast<const uint2*>(sb + kStepGroups * Q * 32 + gu * 32);
 #pragma unroll
         for (int c = 0; c < CG; ++c)
 #pragma unroll
