@@ -80,17 +80,18 @@ KernelFn pick_nibble(int q, bool off, int upw, int nr) {
 
 
 // The sign-plane MFMA kernel for q planes, cg groups of 16 batch rows, an
-// offset term, w waves and non-temporal sign loads, or nullptr.
-KernelFn pick_sign_mfma(int q, int cg, bool off, int w, bool nt) {
+// offset term, w waves, non-temporal sign loads and x staged once per item
+// (xi), or nullptr.
+KernelFn pick_sign_mfma(int q, int cg, bool off, int w, bool nt, bool xi = false) {
   switch (q) {
-    case 1: return sign_mfma_kernel_of_q<1>(cg, off, w, nt);
-    case 2: return sign_mfma_kernel_of_q<2>(cg, off, w, nt);
-    case 3: return sign_mfma_kernel_of_q<3>(cg, off, w, nt);
-    case 4: return sign_mfma_kernel_of_q<4>(cg, off, w, nt);
-    case 5: return sign_mfma_kernel_of_q<5>(cg, off, w, nt);
-    case 6: return sign_mfma_kernel_of_q<6>(cg, off, w, nt);
-    case 7: return sign_mfma_kernel_of_q<7>(cg, off, w, nt);
-    case 8: return sign_mfma_kernel_of_q<8>(cg, off, w, nt);
+    case 1: return sign_mfma_kernel_of_q<1>(cg, off, w, nt, xi);
+    case 2: return sign_mfma_kernel_of_q<2>(cg, off, w, nt, xi);
+    case 3: return sign_mfma_kernel_of_q<3>(cg, off, w, nt, xi);
+    case 4: return sign_mfma_kernel_of_q<4>(cg, off, w, nt, xi);
+    case 5: return sign_mfma_kernel_of_q<5>(cg, off, w, nt, xi);
+    case 6: return sign_mfma_kernel_of_q<6>(cg, off, w, nt, xi);
+    case 7: return sign_mfma_kernel_of_q<7>(cg, off, w, nt, xi);
+    case 8: return sign_mfma_kernel_of_q<8>(cg, off, w, nt, xi);
     default: return nullptr;
   }
 }
@@ -445,6 +446,17 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
   if (c.S < 1) c.S = 1;
   if (c.S > 1 && split_ws_bytes(G, m, c.S) > max_ws) c.S = 1;
   if (c.n_rb * c.n_bg > kMaxCounters) c.S = 1;   // counters live in a fixed region
+  // The sign-plane MFMA kernel stages x once per item instead of once per
+  // input tile (no barrier in its tile loop) where the launch has one group of
+  // 16 batch rows per item, no more items than compute units and at most
+  // kXITiles input tiles per item; LUTGEMM_TILE field XL = 0 declines it.
+  // 12288 x 12288 at m = 4 / 8 / 16 (split 5): see the kernel.
+  if (c.mf) {
+    const int64_t items = c.n_rb * c.n_bg * c.S;
+    const int64_t tiles = (G.KT + c.S - 1) / c.S;
+    c.xl = c.MC == 16 && items <= cus && tiles <= kXITiles && !(have_o && o.xl == 0) &&
+           pick_sign_mfma(q, 1, off, c.W, c.n_bg == 1, true) != nullptr;
+  }
   // batch 1 without x in LDS: each sign byte is still read once per product
   // (where a read-once instance exists for the choice, it differs from the
   // ordinary one)
@@ -542,7 +554,7 @@ int launch(const Geometry& G, int64_t m, const Config& c, int cus, const void* d
            const void* d_alpha, const void* d_offset, const void* d_x, void* d_y, void* ws,
            hipStream_t strm) {
   KernelFn fn = c.us ? pick_nibble((int)G.q, G.has_offset, c.upw, c.nr)
-                : c.mf ? pick_sign_mfma((int)G.q, c.MC / 16, G.has_offset, c.W, c.n_bg == 1)
+                : c.mf ? pick_sign_mfma((int)G.q, c.MC / 16, G.has_offset, c.W, c.n_bg == 1, c.xl)
                        : pick_kernel((int)G.q, c.RPW, c.MC, c.gq, G.has_offset, c.W, c.ring, c.xl,
                                      c.pr, c.ei, c.once);
   if (!fn) return LUTGEMM_ERR_INTERNAL;

@@ -11,5 +11,5 @@
 namespace lutgemm {
 template KernelFn kernels_of_q<LUTGEMM_Q>(int, int, bool, bool, int, int, bool, int, bool, bool);
 template KernelFn nibble_kernel_of_q<LUTGEMM_Q>(bool, int, int);
-template KernelFn sign_mfma_kernel_of_q<LUTGEMM_Q>(int, bool, int, bool);
+template KernelFn sign_mfma_kernel_of_q<LUTGEMM_Q>(int, bool, int, bool, bool);
 }  // namespace lutgemm

@@ -66,20 +66,27 @@ constexpr int kXBufBytes = 16 * CG * kXRowBytes;
 // [group][16 rows] fp16
 template <int Q, bool OFF>
 constexpr int kSBufBytes = kStepGroups * Q * 32 + (OFF ? kStepGroups * 32 : 0);
-template <int Q, int CG, bool OFF, int W>
-constexpr int kSignMfmaLds = kSignTableBytes + 2 * kXBufBytes<CG> + 2 * W * kSBufBytes<Q, OFF>;
+// x of a whole item (XI): the 16 batch rows of up to kXITiles input tiles,
+// rows padded to kXIRowBytes so that the 16 columns of a B read still fall in
+// different banks (row stride = 4 banks mod 64)
+constexpr int kXITiles = 5;
+constexpr int kXIRowBytes = kXITiles * kChunkTile * 16 + 16;
+template <int CG, bool XI>
+constexpr int kXRegion = XI ? 16 * CG * kXIRowBytes : 2 * kXBufBytes<CG>;
+template <int Q, int CG, bool OFF, int W, bool XI = false>
+constexpr int kSignMfmaLds = kSignTableBytes + kXRegion<CG, XI> + 2 * W * kSBufBytes<Q, OFF>;
 
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 // Everything one wave needs from memory for one input tile.
-template <int Q, int CG, bool OFF, int W>
+template <int Q, int CG, bool OFF, int W, bool XI = false>
 struct MfmaTile {
-  static constexpr int NXP = 16 * CG / W;   // x pieces (16 B) this thread stages per tile
+  static constexpr int NXP = XI ? 0 : 16 * CG / W;   // x pieces (16 B) this thread stages per tile
   TilePos pos;
   uint32_t sw[Q][kStepGroups];   // sign bytes of this lane's row: [plane][u], byte b = step 4u + b
-  uint4 xv[NXP];                 // x pieces for the workgroup's staging
+  uint4 xv[NXP > 0 ? NXP : 1];   // x pieces for the workgroup's staging (none with XI)
   uint4 sv;                      // this lane's piece of the wave's scale block
   uint4 ov;                      // ... and of its offset block (lanes 0..7)
 };
@@ -91,10 +98,10 @@ __device__ __forceinline__ int mfma_group(const Params& p, int k) { return group
 // j of thread t is batch row (t + j * 64 W) / 64 of the group, chunk t % 64;
 // scales: lanes 0 .. 8Q-1 load 16 bytes each of the row tile's block from the
 // tile's first group on (the range check zeroes reads past the buffer).
-template <int Q, int CG, bool OFF, int W, bool NT>
+template <int Q, int CG, bool OFF, int W, bool NT, bool XI = false>
 __device__ __forceinline__ void mfma_load(const Params& p, int lane, int wave,
-                                          MfmaTile<Q, CG, OFF, W>& T) {
-  using MT = MfmaTile<Q, CG, OFF, W>;
+                                          MfmaTile<Q, CG, OFF, W, XI>& T) {
+  using MT = MfmaTile<Q, CG, OFF, W, XI>;
   const TilePos& t = T.pos;
   const int k0 = t.kt * kChunkTile * 8;
   const bool rows = t.live && t.c.nrt > 0;   // uniform over the wave
@@ -116,7 +123,7 @@ __device__ __forceinline__ void mfma_load(const Params& p, int lane, int wave,
       T.sw[i][3] = v.w;
     }
   }
-  {
+  if constexpr (!XI) {
     const uint32_t nx = (uint32_t)p.m * (uint32_t)p.K * 2u;
     const auto rs = make_rsrc(p.x, t.live ? nx : 0u);
 #pragma unroll
@@ -166,17 +173,19 @@ __device__ __forceinline__ void mfma_transpose(uint32_t (&v)[4], bool a0, bool a
 }
 
 // Write a loaded tile's x pieces and this wave's scales (offsets) into LDS buffer `buf`.
-template <int Q, int CG, bool OFF, int W>
+template <int Q, int CG, bool OFF, int W, bool XI = false>
 __device__ __forceinline__ void mfma_stage(uint8_t* smem, int buf, int lane, int wave,
-                                           const MfmaTile<Q, CG, OFF, W>& T) {
-  using MT = MfmaTile<Q, CG, OFF, W>;
-  uint8_t* xb = smem + kSignTableBytes + buf * kXBufBytes<CG>;
+                                           const MfmaTile<Q, CG, OFF, W, XI>& T) {
+  using MT = MfmaTile<Q, CG, OFF, W, XI>;
+  if constexpr (!XI) {
+    uint8_t* xb = smem + kSignTableBytes + buf * kXBufBytes<CG>;
 #pragma unroll
-  for (int j = 0; j < MT::NXP; ++j) {
-    const int piece = wave * 64 + lane + j * W * 64;
-    *reinterpret_cast<uint4*>(xb + (piece >> 6) * kXRowBytes + (piece & 63) * 16) = T.xv[j];
+    for (int j = 0; j < MT::NXP; ++j) {
+      const int piece = wave * 64 + lane + j * W * 64;
+      *reinterpret_cast<uint4*>(xb + (piece >> 6) * kXRowBytes + (piece & 63) * 16) = T.xv[j];
+    }
   }
-  uint8_t* sb = smem + kSignTableBytes + 2 * kXBufBytes<CG> + (wave * 2 + buf) * kSBufBytes<Q, OFF>;
+  uint8_t* sb = smem + kSignTableBytes + kXRegion<CG, XI> + (wave * 2 + buf) * kSBufBytes<Q, OFF>;
   if (lane < 8 * Q) *reinterpret_cast<uint4*>(sb + 16 * lane) = T.sv;
   if constexpr (OFF) {
     if (lane < 8) *reinterpret_cast<uint4*>(sb + kStepGroups * Q * 32 + 16 * lane) = T.ov;
@@ -185,18 +194,21 @@ __device__ __forceinline__ void mfma_stage(uint8_t* smem, int buf, int lane, int
 
 // The MFMAs and group scaling of one input tile for this wave's row tile.
 // acc[cg][r]: row 4 * (lane / 16) + r of the row tile, batch row lane % 16 + 16 cg.
-template <int Q, int CG, bool OFF, int W>
+// XI: x of the whole item is staged, the tile at input tile xt of it.
+template <int Q, int CG, bool OFF, int W, bool XI = false>
 __device__ __forceinline__ void mfma_tile(const Params& p, const uint8_t* smem, int buf,
-                                          int lane, int wave, const MfmaTile<Q, CG, OFF, W>& T,
-                                          float (&acc)[CG][4]) {
+                                          int lane, int wave, const MfmaTile<Q, CG, OFF, W, XI>& T,
+                                          float (&acc)[CG][4], int xt = 0) {
   const int k0 = T.pos.kt * kChunkTile * 8;
   const int nu = min(kStepGroups, (p.K - k0) >> 7);   // step groups inside K (K % 128 == 0)
   const int jg = lane >> 4;
   // table copy of this lane: all 16 differ within any 16 consecutive lanes and
   // within lanes l, l + 32 (however the LDS groups the lanes of a 128-bit read)
   const uint32_t cb = (uint32_t)((lane & 15) ^ ((lane >> 2) & 8)) << 4;
-  const uint8_t* xb = smem + kSignTableBytes + buf * kXBufBytes<CG> + (lane & 15) * kXRowBytes + 64 * jg;
-  const uint8_t* sb = smem + kSignTableBytes + 2 * kXBufBytes<CG> +
+  constexpr int kRow = XI ? kXIRowBytes : kXRowBytes;   // bytes per batch row of staged x
+  const uint8_t* xb = XI ? smem + kSignTableBytes + (lane & 15) * kXIRowBytes + xt * (kChunkTile * 16) + 64 * jg
+                         : smem + kSignTableBytes + buf * kXBufBytes<CG> + (lane & 15) * kXRowBytes + 64 * jg;
+  const uint8_t* sb = smem + kSignTableBytes + kXRegion<CG, XI> +
                       (wave * 2 + buf) * kSBufBytes<Q, OFF> + 8 * jg;
   const int grp0 = mfma_group(p, k0);
   const half8v ones = {1, 1, 1, 1, 1, 1, 1, 1};
@@ -228,7 +240,7 @@ __device__ __forceinline__ void mfma_tile(const Params& p, const uint8_t* smem, 
         auto read_step = [&](int b, int slot) {
 #pragma unroll
           for (int c = 0; c < CG; ++c)
-            B[slot][c] = *reinterpret_cast<const half8v*>(xb + c * 16 * kXRowBytes + 256 * u + 16 * b);
+            B[slot][c] = *reinterpret_cast<const half8v*>(xb + c * 16 * kRow + 256 * u + 16 * b);
           const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)b) << 8);
 #pragma unroll
           for (int i = 0; i < Q; ++i)
@@ -261,7 +273,7 @@ __device__ __forceinline__ void mfma_tile(const Params& p, const uint8_t* smem, 
           half8v B[CG];
 #pragma unroll
           for (int c = 0; c < CG; ++c)
-            B[c] = *reinterpret_cast<const half8v*>(xb + c * 16 * kXRowBytes + 256 * u + 16 * b);
+            B[c] = *reinterpret_cast<const half8v*>(xb + c * 16 * kRow + 256 * u + 16 * b);
           const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)b) << 8);
 #pragma unroll
           for (int i = 0; i < Q; ++i) {
@@ -400,18 +412,59 @@ __device__ __forceinline__ void mfma_split_epilogue(const Params& p, int* s_last
   }
 }
 
+// XI: x of a workgroup's item, batch rows r0 .. r0 + 15 over its input tiles
+// kt .. kt1 - 1 (at most kXITiles), loaded by every thread (piece j of thread
+// t: index t + 64 W j = (row, tile, chunk) in that order; zero past the batch,
+// the item's tiles and K) and written once into the x region.
+template <int W>
+constexpr int kXIPieces = 16 * kXITiles * 64 / (W * 64);
+
+template <int W>
+__device__ __forceinline__ void mfma_item_x_load(const Params& p, const TilePos& t, uint4 (&xr)[kXIPieces<W>]) {
+  const uint32_t nx = (uint32_t)p.m * (uint32_t)p.K * 2u;
+  const auto rs = make_rsrc(p.x, t.live ? nx : 0u);
+  const int nt = t.c.kt1 - t.kt;
+#pragma unroll
+  for (int j = 0; j < kXIPieces<W>; ++j) {
+    const int idx = (int)threadIdx.x + j * W * 64;
+    const int row = idx / (kXITiles * 64);
+    const int rem = idx - row * (kXITiles * 64);
+    const int tt = rem >> 6, chunk = rem & 63;
+    const int k = (t.kt + tt) * kChunkTile * 8 + 8 * chunk;
+    const bool ok = row < t.c.rows_here && tt < nt && k < p.K;
+    const uint32_t off = ((uint32_t)(t.c.r0 + row) * (uint32_t)p.K + (uint32_t)k) * 2u;
+    xr[j] = load16(rs, ok ? off : 0xFFFFFFF0u);
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void mfma_item_x_store(uint8_t* smem, const uint4 (&xr)[kXIPieces<W>]) {
+#pragma unroll
+  for (int j = 0; j < kXIPieces<W>; ++j) {
+    const int idx = (int)threadIdx.x + j * W * 64;
+    const int row = idx / (kXITiles * 64);
+    const int rem = idx - row * (kXITiles * 64);
+    *reinterpret_cast<uint4*>(smem + kSignTableBytes + row * kXIRowBytes + (rem >> 6) * (kChunkTile * 16) +
+                              (rem & 63) * 16) = xr[j];
+  }
+}
+
 // Persistent kernel: workgroup b processes items b, b + gridDim.x, ...; an
 // item is (row block of W row tiles, split of the input tiles, group of 16 CG
 // batch rows). While one tile's MFMAs run, the next two tiles' loads are in
 // flight. NT: every sign byte is read once per product (one batch group), and
-// those loads are non-temporal.
-template <int Q, int CG, bool OFF, int W, bool NT>
+// those loads are non-temporal. XI (one group of 16 batch rows, one item per
+// workgroup, at most kXITiles input tiles per item): x of the whole item is
+// staged in LDS once, at the start, and the tile loop has no barrier (no LDS
+// written by one wave is read by another after the start).
+template <int Q, int CG, bool OFF, int W, bool NT, bool XI = false>
 __global__ void __launch_bounds__(W * 64, W / 4)
     __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) sign_mfma_kernel(Params p) {
   static_assert(16 * CG % W == 0, "x pieces per thread");
+  static_assert(!XI || CG == 1, "x per item: one group of 16 batch rows");
   constexpr int MC = 16 * CG;
-  using MT = MfmaTile<Q, CG, OFF, W>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSignMfmaLds<Q, CG, OFF, W>];
+  using MT = MfmaTile<Q, CG, OFF, W, XI>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSignMfmaLds<Q, CG, OFF, W, XI>];
   LUTGEMM_PHASE(0);
   LUTGEMM_PHASE_FLAG(traced_staged);
   LUTGEMM_PHASE_FLAG(traced_step);
@@ -422,11 +475,16 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   // two tiles are in flight (a tile's loads have two tiles' MFMAs to arrive).
   MT S[3];
   S[0].pos = first_tile<1, MC, W>(p, wave, blockIdx.x);
-  mfma_load<Q, CG, OFF, W, NT>(p, lane, wave, S[0]);
+  // XI: the item's x first, so that staging it waits for nothing else
+  uint4 xr[XI ? kXIPieces<W> : 1];
+  if constexpr (XI) mfma_item_x_load<W>(p, S[0].pos, xr);
+  mfma_load<Q, CG, OFF, W, NT, XI>(p, lane, wave, S[0]);
   asm volatile("" ::: "memory");
   if (!S[0].pos.live) return;
+  const int kt0 = S[0].pos.kt;   // XI: the staged item's first input tile
   S[1].pos = next_tile<1, MC, W>(p, wave, S[0].pos);
-  mfma_load<Q, CG, OFF, W, NT>(p, lane, wave, S[1]);
+  if constexpr (XI) S[1].pos.live = S[1].pos.live && S[1].pos.c.item == (int)blockIdx.x;
+  mfma_load<Q, CG, OFF, W, NT, XI>(p, lane, wave, S[1]);
 
   // The sign table: entry v (a sign byte) copy c at byte 256 v + 16 c, its 8
   // fp16 values +1.0 where bit e of v is set and -1.0 elsewhere (bit e is
@@ -443,6 +501,10 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     *reinterpret_cast<uint4*>(smem + 16 * e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   }
   LUTGEMM_PHASE(2);
+  if constexpr (XI) {
+    mfma_item_x_store<W>(smem, xr);
+    __syncthreads();   // the table and the item's x, for every wave
+  }
 
   float acc[CG][4];
 #pragma unroll
@@ -464,7 +526,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   MT cur;
   int buf = 0;
   auto trip = [&](MT& st, MT& ld, const TilePos& after) {
-    mfma_stage<Q, CG, OFF, W>(smem, buf, lane, wave, st);
+    mfma_stage<Q, CG, OFF, W, XI>(smem, buf, lane, wave, st);
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
 #pragma unroll
@@ -476,11 +538,14 @@ __global__ void __launch_bounds__(W * 64, W / 4)
     }
     cur.pos = st.pos;
     ld.pos = next_tile<1, MC, W>(p, wave, after);
-    mfma_load<Q, CG, OFF, W, NT>(p, lane, wave, ld);
-    __syncthreads();
+    // XI: a workgroup's one item (the launch has no more items than workgroups)
+    if constexpr (XI) ld.pos.live = ld.pos.live && ld.pos.c.item == (int)blockIdx.x;
+    mfma_load<Q, CG, OFF, W, NT, XI>(p, lane, wave, ld);
+    if constexpr (!XI) __syncthreads();
     LUTGEMM_PHASE_ONCE(1, traced_staged);
     if (cur.pos.live) {
-      if (cur.pos.c.nrt > 0) mfma_tile<Q, CG, OFF, W>(p, smem, buf, lane, wave, cur, acc);
+      if (cur.pos.c.nrt > 0)
+        mfma_tile<Q, CG, OFF, W, XI>(p, smem, buf, lane, wave, cur, acc, cur.pos.kt - kt0);
       if (cur.pos.kt + 1 == cur.pos.c.kt1) mfma_finish<CG>(p, lane, cur.pos.c, acc);
     }
     LUTGEMM_PHASE_ONCE(3, traced_step);
@@ -505,13 +570,22 @@ constexpr bool kMfmaFits =
     W == 16 ? (CG == 1 ? Q + OFF <= 4 : Q + OFF <= 2) : (CG == 1 || Q + OFF <= 7);
 
 // The instance for q planes, cg groups of 16 batch rows, an offset term, w
-// waves and non-temporal sign loads (nt), or nullptr where none is built
-// (see kMfmaFits).
+// waves, non-temporal sign loads (nt) and x staged once per item (xi), or
+// nullptr where none is built (see kMfmaFits; xi needs cg = 1 and the LDS for
+// kXITiles input tiles of x).
 template <int Q>
-KernelFn sign_mfma_kernel_of_q(int cg, bool off, int w, bool nt) {
+KernelFn sign_mfma_kernel_of_q(int cg, bool off, int w, bool nt, bool xi) {
 #define LUTGEMM_SM(CG, OFF, W)                                                           \
   if constexpr (kSignMfmaLds<Q, CG, OFF, W> <= 160 * 1024 &&                               \
                 kMfmaFits<Q, CG, OFF, W>) {                                                \
+    if (xi) {                                                                             \
+      if constexpr (CG == 1 && kSignMfmaLds<Q, CG, OFF, W, true> <= 160 * 1024) {          \
+        return nt ? sign_mfma_kernel<Q, CG, OFF, W, true, true>                           \
+                  : sign_mfma_kernel<Q, CG, OFF, W, false, true>;                         \
+      } else {                                                                            \
+        return nullptr;                                                                   \
+      }                                                                                   \
+    }                                                                                     \
     return nt ? sign_mfma_kernel<Q, CG, OFF, W, true> : sign_mfma_kernel<Q, CG, OFF, W, false>; \
   } else {                                                                                \
     return nullptr;                                                                       \
@@ -533,13 +607,13 @@ KernelFn sign_mfma_kernel_of_q(int cg, bool off, int w, bool nt) {
   return nullptr;
 }
 
-extern template KernelFn sign_mfma_kernel_of_q<1>(int, bool, int, bool);
-extern template KernelFn sign_mfma_kernel_of_q<2>(int, bool, int, bool);
-extern template KernelFn sign_mfma_kernel_of_q<3>(int, bool, int, bool);
-extern template KernelFn sign_mfma_kernel_of_q<4>(int, bool, int, bool);
-extern template KernelFn sign_mfma_kernel_of_q<5>(int, bool, int, bool);
-extern template KernelFn sign_mfma_kernel_of_q<6>(int, bool, int, bool);
-extern template KernelFn sign_mfma_kernel_of_q<7>(int, bool, int, bool);
-extern template KernelFn sign_mfma_kernel_of_q<8>(int, bool, int, bool);
+extern template KernelFn sign_mfma_kernel_of_q<1>(int, bool, int, bool, bool);
+extern template KernelFn sign_mfma_kernel_of_q<2>(int, bool, int, bool, bool);
+extern template KernelFn sign_mfma_kernel_of_q<3>(int, bool, int, bool, bool);
+extern template KernelFn sign_mfma_kernel_of_q<4>(int, bool, int, bool, bool);
+extern template KernelFn sign_mfma_kernel_of_q<5>(int, bool, int, bool, bool);
+extern template KernelFn sign_mfma_kernel_of_q<6>(int, bool, int, bool, bool);
+extern template KernelFn sign_mfma_kernel_of_q<7>(int, bool, int, bool, bool);
+extern template KernelFn sign_mfma_kernel_of_q<8>(int, bool, int, bool, bool);
 
 }  // namespace lutgemm

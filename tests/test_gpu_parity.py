@@ -360,6 +360,36 @@ def test_sign_mfma_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# The sign-plane MFMA kernel with x staged once per item (XL = 1 where its
+# conditions hold: one group of 16 batch rows, no more items than CUs, at most
+# five input tiles per item): ragged rows and batches, a last input tile of one
+# step group, offsets, groups straddling input tiles, 8-wave instances (q = 5)
+@pytest.mark.parametrize("tile,N,K,q,g,m,off", [
+    ("1,3,16,16,0,0,1,5", 1000, 4224, 3, 128, 4, False),
+    ("1,2,0,0,0,0,1,5", 1000, 4224, 3, 128, 4, False),     # five tiles per item
+    ("1,0,0,0,0,0,1,5", 300, 1536, 2, 256, 12, True),
+    ("1,2,16,16,0,0,1,5", 513, 4096, 3, 128, 16, False),
+    ("1,4,0,0,0,0,1,5", 129, 3072, 1, 384, 7, True),
+    ("1,1,0,0,0,0,1,5", 64, 512, 3, 128, 3, False),
+    ("1,3,8,0,0,0,1,5", 2048, 2560, 5, 128, 9, False),
+    ("", 4096, 12288, 3, 128, 5, False),                    # the default launch
+])
+def test_sign_mfma_x_per_item_all_outputs(monkeypatch, tile, N, K, q, g, m, off):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=3 * N + q + m, with_offset=off,
+                             name=f"signmfma_xi_{N}x{K}q{q}g{g}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    monkeypatch.setenv("LUTGEMM_TILE", tile)
+    plan = lg.query_plan(N, K, q, g, off, m)
+    assert plan["tables"] == "sign_mfma" and plan["x_in_lds"] == 1, plan
+    _say(f"sign MFMA, x per item {tile}: N={N} K={K} q={q} g={g} m={m} offset={off} plan={plan}")
+    _check(_gpu_y(pw, w.x), w)
+    # and the same product with x staged per input tile
+    monkeypatch.setenv("LUTGEMM_TILE", (tile or "1,0,0,0,0,0,1,5").replace(",1,5", ",0,5"))
+    assert lg.query_plan(N, K, q, g, off, m)["x_in_lds"] == 0
+    _check(_gpu_y(pw, w.x), w)
+    monkeypatch.delenv("LUTGEMM_TILE")
+
+
 # "RPW,S,W,MC,ring,RI,XL,PR,EI": x in LDS with the early-issue ring (EI = 1), forced
 # onto single-item, split and many-item launches, and the plain ring beside it (EI = 0)
 @pytest.mark.parametrize("tile", ["1,1,16,1,0,12,1,0,1", "1,1,16,1,0,12,1,0,0", "1,3,16,1,0,5,1,0,1",
