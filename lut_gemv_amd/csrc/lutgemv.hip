@@ -438,9 +438,21 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
   // on 12288 x 12288 it measured 28.7 / 29.6 / 32.2 / 53.4 us at m = 4 / 8 /
   // 16 / 32 against 33.2 / 51.9 / 93.0 / 170.4 us for the best table launch;
   // at m = 2 the paired tables stay faster (21.2 against 28.1 us).
+  // Past 16 batch rows, where 32-row items pad the batch no more than 16-row
+  // ones and the 8-wave instance reads its operands a step ahead (at most 3
+  // planes, the offset counted as one), 8 waves with 32 batch rows per item:
+  // each sign vector then serves two MFMAs. Measured against 16 waves x 16
+  // rows: 12288 x 12288 q = 3 at m = 24 / 32 / 64 43.1 / 44.2 / 75.8 against
+  // 48.3 / 48.7 / 84.3 us, q = 2 at m = 32 36.2 against 40.2, 49152 x 12288
+  // and 12288 x 49152 at m = 32 125.7 / 125.1 against 151.9 / 151.7; not at
+  // m = 48 (75.6 against 66.0, the second group half empty) or q = 4 (58.8
+  // against 58.0, no read-ahead).
   if (!have_o && m >= 4) {
     Config f{};
-    if (mfma_config(G, m, cus, max_ws, 16, 1, 0, &f) || mfma_config(G, m, cus, max_ws, 8, 1, 0, &f))
+    const bool cg2 = m > 16 && (m + 31) / 32 * 32 <= (m + 15) / 16 * 16 &&
+                     (q + (off ? 1 : 0)) * 2 <= 6;
+    if ((cg2 && mfma_config(G, m, cus, max_ws, 8, 2, 0, &f)) ||
+        mfma_config(G, m, cus, max_ws, 16, 1, 0, &f) || mfma_config(G, m, cus, max_ws, 8, 1, 0, &f))
       c = f;
   }
   if (c.S < 1) c.S = 1;

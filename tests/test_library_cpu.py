@@ -121,10 +121,13 @@ def test_query_plan_batch_one_and_batched():
         p = lg.query_plan(12288, 12288, 3, 128, False, m)
         if m == 2:
             assert p["tables"] == "paired_mfma" and p["batch_rows"] == 2 and p["x_in_lds"] == 0, p
-        else:   # the sign-plane MFMA kernel from 4 batch rows on
+        elif m <= 16:   # the sign-plane MFMA kernel from 4 batch rows on
             assert p["tables"] == "sign_mfma" and p["batch_rows"] == 16 and p["waves"] == 16, p
-            S = 5 if m <= 16 else 2   # measured best: 28.7 us at m = 4, 53.4 at m = 32
-            assert p["split"] == S and p["items"] == 48 * S * -(-m // 16), p
+            assert p["split"] == 5 and p["items"] == 48 * 5, p   # measured best at m = 4
+            assert p["x_in_lds"] == 1, p                          # x staged once per item
+        else:           # 8 waves x 32 batch rows per item past 16 rows (q <= 3)
+            assert p["tables"] == "sign_mfma" and p["batch_rows"] == 32 and p["waves"] == 8, p
+            assert p["split"] == 2 and p["items"] == 96 * 2, p
         assert p["workspace_bytes"] == lg.workspace_size(12288, 12288, 3, 128, False, m)
         assert p["workgroups"] == min(p["items"], 256)
     # scale groups that are not whole 128-input step groups keep the tables
