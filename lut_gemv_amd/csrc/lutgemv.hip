@@ -433,8 +433,8 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
     }
     if (o.s >= 1) c.S = (int)(o.s < G.KT ? o.s : (G.KT > 0 ? G.KT : 1));
   }
-  // From 4 batch rows on, with scale groups of whole 128-input step groups,
-  // the sign-plane MFMA kernel (16 waves, 16 batch rows per item where built):
+  // With scale groups of whole 128-input step groups, the sign-plane MFMA
+  // kernel (16 waves, 16 batch rows per item where built):
   // on 12288 x 12288 it measured 28.7 / 29.6 / 32.2 / 53.4 us at m = 4 / 8 /
   // 16 / 32 against 33.2 / 51.9 / 93.0 / 170.4 us for the best table launch;
   // at m = 2 the paired tables stay faster (21.2 against 28.1 us).
@@ -447,7 +447,16 @@ Config choose_config(const Geometry& G, int64_t m, int cus, size_t max_ws,
   // and 12288 x 49152 at m = 32 125.7 / 125.1 against 151.9 / 151.7; not at
   // m = 48 (75.6 against 66.0, the second group half empty) or q = 4 (58.8
   // against 58.0, no read-ahead).
-  if (!have_o && m >= 4) {
+  // From 3 batch rows on where the matrix holds at least 6144 (row tile,
+  // input tile) units, and from 6 on always: on smaller matrices at m = 3..5
+  // the table launches are faster (the sign table and the fill are fixed costs
+  // that few tiles per CU do not amortise). Measured, tables against the
+  // sign-plane MFMA kernel: at m = 3 4096 x 4096 9.8 / 13.5 us, 5120 x 5120
+  // 11.6 / 14.9, 4096 x 11008 15.0 / 16.6, but 12288 x 4096 17.9 / 15.3,
+  // 12288 x 12288 33.7 / 25.2, 49152 x 12288 107.7 / 85.0; at m = 4 4096 x
+  // 11008 14.8 / 16.7, 4096 x 14336 18.8 / 17.7; at m = 6 and 8 4096 x 4096
+  // within 2%, 4096 x 11008 19.0 / 16.8 and 21.1 / 17.0.
+  if (!have_o && m >= 3 && (m >= 6 || G.RT * G.KT >= 6144)) {
     Config f{};
     const bool cg2 = m > 16 && (m + 31) / 32 * 32 <= (m + 15) / 16 * 16 &&
                      (q + (off ? 1 : 0)) * 2 <= 6;

@@ -132,6 +132,12 @@ def test_query_plan_batch_one_and_batched():
         assert p["workgroups"] == min(p["items"], 256)
     # scale groups that are not whole 128-input step groups keep the tables
     assert lg.query_plan(12288, 12288, 3, 64, False, 8)["tables"] != "sign_mfma"
+    # the matrix cores from 3 batch rows on for matrices of >= 6144 (row tile,
+    # input tile) units, from 6 on for all; the tables below that (measured)
+    for (N, K, m, mf) in ((12288, 12288, 3, True), (12288, 4096, 3, True), (4096, 14336, 4, True),
+                          (4096, 4096, 3, False), (4096, 11008, 4, False), (5120, 5120, 5, False),
+                          (4096, 4096, 6, True), (12288, 12288, 2, False)):
+        assert (lg.query_plan(N, K, 3, 128, False, m)["tables"] == "sign_mfma") == mf, (N, K, m)
     nib = lg.query_plan(4096, 4096, 3, 128, False, 1)
     assert nib["tables"] == "nibble" and nib["split"] == 1 and nib["workgroups"] == nib["items"]
     # batch 1 with a split: row blocks of 8-16 row tiles sized so that the
