@@ -419,6 +419,16 @@ __device__ __forceinline__ void mfma_split_epilogue(const Params& p, int* s_last
 template <int W>
 constexpr int kXIPieces = 16 * kXITiles * 64 / (W * 64);
 
+// XI: the tile after t within the workgroup's one item, dead past its end.
+// Every register set then holds the same item state (the same values, kept
+// once), instead of what a move to another item would need.
+__device__ __forceinline__ TilePos xi_next_tile(const TilePos& t) {
+  TilePos n = t;
+  n.kt = t.kt + 1;
+  n.live = t.live && n.kt < t.c.kt1;
+  return n;
+}
+
 template <int W>
 __device__ __forceinline__ void mfma_item_x_load(const Params& p, const TilePos& t, uint4 (&xr)[kXIPieces<W>]) {
   const uint32_t nx = (uint32_t)p.m * (uint32_t)p.K * 2u;
@@ -482,8 +492,7 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   asm volatile("" ::: "memory");
   if (!S[0].pos.live) return;
   const int kt0 = S[0].pos.kt;   // XI: the staged item's first input tile
-  S[1].pos = next_tile<1, MC, W>(p, wave, S[0].pos);
-  if constexpr (XI) S[1].pos.live = S[1].pos.live && S[1].pos.c.item == (int)blockIdx.x;
+  S[1].pos = XI ? xi_next_tile(S[0].pos) : next_tile<1, MC, W>(p, wave, S[0].pos);
   mfma_load<Q, CG, OFF, W, NT, XI>(p, lane, wave, S[1]);
 
   // The sign table: entry v (a sign byte) copy c at byte 256 v + 16 c, its 8
@@ -551,9 +560,8 @@ __global__ void __launch_bounds__(W * 64, W / 4)
       mfma_transpose(cur.sw[i], lane & 1, lane & 2);
     }
     cur.pos = st.pos;
-    ld.pos = next_tile<1, MC, W>(p, wave, after);
     // XI: a workgroup's one item (the launch has no more items than workgroups)
-    if constexpr (XI) ld.pos.live = ld.pos.live && ld.pos.c.item == (int)blockIdx.x;
+    ld.pos = XI ? xi_next_tile(after) : next_tile<1, MC, W>(p, wave, after);
     mfma_load<Q, CG, OFF, W, NT, XI>(p, lane, wave, ld);
     if constexpr (!XI) __syncthreads();
     LUTGEMM_PHASE_ONCE(1, traced_staged);
