@@ -148,9 +148,13 @@ bool tile_override(TileOverride* o) {
 // w waves of one row tile each per row block, cg groups of 16 batch rows per
 // item, and the split of the input tiles s_force, or (s_force < 1) the split
 // that gives the busiest CU the fewest tile steps, each item also paying about
-// two tile steps for its pipeline fill and a split two more for its reduction
+// one tile step for its pipeline fill and a split two more for its reduction
 // (measured on 12288 x 12288 at m = 4: 85.3 us unsplit on 48 CUs, splits 2, 3,
-// 4, 5, 8: 49.8, 37.1, 30.8, 28.7, 36.4 us).
+// 4, 5, 8: 49.8, 37.1, 30.8, 28.7, 36.4 us; on 49152 x 12288 at m = 4, splits
+// 1, 2, 4, 5: 84.6, 89.5, 74.9, 77.6 us. A charge of two steps per item had
+// kept 49152 x 12288 unsplit on 192 of the 256 CUs; with one it takes split 4
+// there, 74.1 against 84.9 us at m = 4, 81.8 against 86.7 at m = 16, and
+// 12288 x 12288 at m = 32 split 5, 42.6 against 44.1 us).
 // Sign loads are non-temporal when one batch group reads the weights once.
 bool mfma_config(const Geometry& G, int64_t m, int cus, size_t max_ws, int w, int cg,
                  int64_t s_force, Config* out) {
@@ -174,7 +178,7 @@ bool mfma_config(const Geometry& G, int64_t m, int cus, size_t max_ws, int w, in
       const int64_t items = n_rb * n_bg * s;
       const int64_t per_cu = (items + cus - 1) / cus;
       const int64_t tiles = (G.KT + s - 1) / s;
-      const double cost = (double)per_cu * ((double)tiles + 2.0) + (s > 1 ? 2.0 : 0.0);
+      const double cost = (double)per_cu * ((double)tiles + 1.0) + (s > 1 ? 2.0 : 0.0);
       if (cost < best - 1e-9) {
         best = cost;
         best_s = s;

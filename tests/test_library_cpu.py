@@ -127,7 +127,7 @@ def test_query_plan_batch_one_and_batched():
             assert p["x_in_lds"] == 1, p                          # x staged once per item
         else:           # 8 waves x 32 batch rows per item past 16 rows (q <= 3)
             assert p["tables"] == "sign_mfma" and p["batch_rows"] == 32 and p["waves"] == 8, p
-            assert p["split"] == 2 and p["items"] == 96 * 2, p
+            assert p["split"] == 5 and p["items"] == 96 * 5, p   # measured: 42.6 us, split 2 44.1
         assert p["workspace_bytes"] == lg.workspace_size(12288, 12288, 3, 128, False, m)
         assert p["workgroups"] == min(p["items"], 256)
     # scale groups that are not whole 128-input step groups keep the tables
