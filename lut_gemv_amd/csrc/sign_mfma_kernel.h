@@ -412,10 +412,7 @@ __device__ __forceinline__ void mfma_split_epilogue(const Params& p, int* s_last
   }
 }
 
-// XI: x of a workgroup's item, batch rows r0 .. r0 + 15 over its input tiles
-// kt .. kt1 - 1 (at most kXITiles), loaded by every thread (piece j of thread
-// t: index t + 64 W j = (row, tile, chunk) in that order; zero past the batch,
-// the item's tiles and K) and written once into the x region.
+// XI: 16-byte pieces of an item's x per thread
 template <int W>
 constexpr int kXIPieces = 16 * kXITiles * 64 / (W * 64);
 
@@ -429,6 +426,10 @@ __device__ __forceinline__ TilePos xi_next_tile(const TilePos& t) {
   return n;
 }
 
+// XI: x of a workgroup's item, batch rows r0 .. r0 + 15 over its input tiles
+// kt .. kt1 - 1 (at most kXITiles), loaded by every thread (piece j of thread
+// t: index t + 64 W j = (row, tile, chunk) in that order; zero past the batch,
+// the item's tiles and K) and written once into the x region.
 template <int W>
 __device__ __forceinline__ void mfma_item_x_load(const Params& p, const TilePos& t, uint4 (&xr)[kXIPieces<W>]) {
   const uint32_t nx = (uint32_t)p.m * (uint32_t)p.K * 2u;
@@ -524,8 +525,8 @@ __global__ void __launch_bounds__(W * 64, W / 4)
   // One input tile per trip: stage the oldest loaded tile into buffer `buf`
   // (once it is staged its loads are complete: x and the scales are its last
   // loads), issue the loads of the tile two ahead into the set just staged,
-  // wait at the barrier, then the staged tile's MFMAs and, at its item's end,
-  // the store. The buffer written here was last read two trips ago, before
+  // wait at the barrier (none with XI: only the wave's own scales are staged),
+  // then the staged tile's MFMAs and, at its item's end, the store. The buffer written here was last read two trips ago, before
   // the previous barrier. Tiles past the workgroup's last are dead: their
   // loads touch no memory, zeros are staged and nothing is computed, so the
   // loop runs whole rounds of three trips and its one exit is at its head;
