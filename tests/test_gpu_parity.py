@@ -390,6 +390,26 @@ def test_sign_mfma_x_per_item_all_outputs(monkeypatch, tile, N, K, q, g, m, off)
     monkeypatch.delenv("LUTGEMM_TILE")
 
 
+# The dispatcher's own batched launches: the sign-plane MFMA kernel from 3 batch
+# rows on larger matrices (x per item), 8 waves x 32 batch rows per item past 16
+# rows (with an offset, scale groups of 256), the tables for a small matrix at 3
+@pytest.mark.parametrize("N,K,q,g,m,off,tables,batch_rows", [
+    (12288, 4096, 3, 128, 3, False, "sign_mfma", 16),
+    (6144, 8192, 3, 128, 5, False, "sign_mfma", 16),
+    (4096, 12288, 3, 256, 20, False, "sign_mfma", 32),
+    (3072, 8192, 2, 128, 64, True, "sign_mfma", 32),
+    (4096, 4096, 3, 128, 3, False, "single", 1),
+])
+def test_batched_default_launches_all_outputs(N, K, q, g, m, off, tables, batch_rows):
+    w = workloads.random_bcq(N, K, q, g, m=m, seed=N + K + m, with_offset=off,
+                             name=f"batched_{N}x{K}q{q}g{g}m{m}")
+    pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g)
+    plan = lg.query_plan(N, K, q, g, off, m)
+    assert plan["tables"] == tables and plan["batch_rows"] == batch_rows, plan
+    _say(f"batched default launch: N={N} K={K} q={q} g={g} m={m} offset={off} plan={plan}")
+    _check(_gpu_y(pw, w.x), w)
+
+
 # "RPW,S,W,MC,ring,RI,XL,PR,EI": x in LDS with the early-issue ring (EI = 1), forced
 # onto single-item, split and many-item launches, and the plain ring beside it (EI = 0)
 @pytest.mark.parametrize("tile", ["1,1,16,1,0,12,1,0,1", "1,1,16,1,0,12,1,0,0", "1,3,16,1,0,5,1,0,1",
