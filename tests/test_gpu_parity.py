@@ -128,6 +128,24 @@ def test_llama7b_int4_uniform_all_outputs():
     _check(y, wb, rows=_sample_rows(w.N, 1024))
 
 
+@pytest.mark.parametrize("m", [8, 24])
+def test_llama7b_int4_uniform_batched(m):
+    """The int4 MLP at batch 8 and 24: the sign-plane MFMA kernel at 8 waves with
+    the offset plane (x per item at 8), against the dequantized definition."""
+    w0 = workloads.generate("llama7b_mlp_int4")
+    x = np.random.default_rng(60 + m).standard_normal((m, w0.K)).astype(np.float16)
+    plan = lg.query_plan(w0.N, w0.K, w0.q, w0.g, True, m)
+    assert plan["tables"] == "sign_mfma" and plan["waves"] == 8, plan
+    _say(f"llama7b int4 at m={m}: plan={plan}")
+    pw = lg.PackedBCQ.from_uniform(w0.codes, w0.scale, w0.zero, w0.q, w0.g)
+    y = _gpu_y(pw, x)
+    Wd = oracle.dequant_uniform(w0.codes, w0.scale, w0.zero, w0.g)
+    x64 = x.astype(np.float64)
+    ok, worst = oracle.parity_ok(y.astype(np.float64), x64 @ Wd.T, np.abs(x64) @ np.abs(Wd).T)
+    _say(f"llama7b int4 at m={m} vs dequantized definition: worst {worst:.3f}")
+    assert ok
+
+
 @pytest.mark.parametrize("m", [4, 16, 32])
 def test_decode_batch_all_outputs(m):
     w = workloads.generate(f"decode_m{m}")
