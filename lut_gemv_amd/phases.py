@@ -31,6 +31,8 @@ def main(argv=None) -> int:
     ap.add_argument("--launches", type=int, default=6)
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--json", action="store_true", help="print one JSON line instead of a table")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="distinct weight copies cycled through (0: enough for >= 4 GiB)")
     args = ap.parse_args(argv)
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
@@ -52,7 +54,7 @@ def main(argv=None) -> int:
     else:
         pw = lg.PackedBCQ.from_bcq(w.bits, w.alpha, w.offset, w.g, device=dev)
     wbytes = pw.d_bits.numel() + 2 * pw.d_alpha.numel() + (2 * pw.d_offset.numel() if pw.has_offset else 0)
-    R = min(512, max(2, -(-(4 << 30) // wbytes)))
+    R = args.rotate if args.rotate > 0 else min(512, max(2, -(-(4 << 30) // wbytes)))
     copies = [pw] + [lg.PackedBCQ(w.N, w.K, w.q, w.g, pw.d_bits.clone(), pw.d_alpha.clone(),
                                   pw.d_offset.clone() if pw.has_offset else None)
                      for _ in range(R - 1)]
